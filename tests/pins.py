@@ -1,0 +1,317 @@
+"""Pins for the CPU oracle: checks against facts the pages and the mathematics
+fix, written so that a plausible mistake in the oracle (a dropped term, a wrong
+sign or index, a transposed operand, another Hadamard ordering, a swapped
+nibble, a wrong clamp) fails at least one of them.
+
+Each check takes the function(s) under test as arguments and raises
+AssertionError on failure. tests/test_oracle.py runs them on the oracle;
+tests/test_controls.py runs them on deliberately broken copies and expects
+them to fail.
+"""
+
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load_matrix(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append([float(t) for t in line.split()])
+    return np.array(rows)
+
+
+# --------------------------------------------------------------------------- H
+def check_hadamard(hadamard_matrix):
+    """Closed form and construction of the order-256 Sylvester matrix.
+
+    * the order-8 matrix equals the textbook table in golden/sylvester_h8.txt;
+    * the order-256 matrix equals the Sylvester doubling H_2n = [[H, H], [H, -H]]
+      built here independently with Kronecker products;
+    * it is symmetric, has entries +-1 and H . H^T = 256 I.
+    """
+    h8 = hadamard_matrix(8)
+    assert np.array_equal(h8, _load_matrix("sylvester_h8.txt")), "H8 differs from the textbook table"
+    h = np.array([[1.0]])
+    h2 = np.array([[1.0, 1.0], [1.0, -1.0]])
+    for _ in range(8):
+        h = np.kron(h2, h)
+    got = hadamard_matrix(256)
+    assert got.shape == (256, 256)
+    assert np.array_equal(got, h), "order-256 matrix is not the Sylvester doubling"
+    assert np.array_equal(got, got.T), "not symmetric"
+    assert np.all(np.abs(got) == 1.0), "entries must be +-1"
+    assert np.array_equal(got @ got.T, 256.0 * np.eye(256)), "H H^T != 256 I"
+
+
+# -------------------------------------------------------------------- rotation
+def _butterfly_fwht(v):
+    """Independent in-place fast Walsh-Hadamard transform of one 256-vector
+    (natural order), scaled by 1/16. Used only to cross-check the oracle's
+    dense product on dyadic inputs, where both are exact."""
+    a = [float(t) for t in v]
+    h = 1
+    while h < len(a):
+        for i in range(0, len(a), 2 * h):
+            for j in range(i, i + h):
+                x, y = a[j], a[j + h]
+                a[j], a[j + h] = x + y, x - y
+        h *= 2
+    return np.array(a) / 16.0
+
+
+def check_rotation(rotate_groups, hadamard_matrix, seed=11):
+    rng = np.random.default_rng(seed)
+    H = hadamard_matrix(256)
+    # Special cases with closed forms.
+    ones = np.ones((1, 256))
+    e0 = np.zeros((1, 256)); e0[0, 0] = 16.0
+    assert np.array_equal(rotate_groups(ones), e0), "1 . Q must be 16 e0"
+    for j in (0, 1, 5, 128, 255):
+        ej = np.zeros((1, 256)); ej[0, j] = 1.0
+        assert np.array_equal(rotate_groups(ej)[0], H[j] / 16.0), "e_j . Q must be H[j]/16"
+        hi = H[j][None, :]
+        ek = np.zeros((1, 256)); ek[0, j] = 16.0
+        assert np.array_equal(rotate_groups(hi), ek), "H[j] . Q must be 16 e_j"
+    # Exact agreement with an independent butterfly FWHT on dyadic integers.
+    x = rng.integers(-1000, 1000, size=(3, 512)).astype(np.float64)
+    got = rotate_groups(x)
+    for r in range(3):
+        for g in range(2):
+            ref = _butterfly_fwht(x[r, 256 * g:256 * (g + 1)])
+            assert np.array_equal(got[r, 256 * g:256 * (g + 1)], ref), "rotation != butterfly FWHT"
+    # Group locality: a vector supported on one group stays in that group.
+    v = np.zeros((1, 768)); v[0, 256:512] = rng.standard_normal(256)
+    rv = rotate_groups(v)
+    assert np.all(rv[0, :256] == 0) and np.all(rv[0, 512:] == 0), "rotation leaks across groups"
+    # Involution (Q Q = I) and norm preservation per group.
+    y = rng.standard_normal((4, 768))
+    back = rotate_groups(rotate_groups(y))
+    assert np.max(np.abs(back - y)) <= 1e-13 * np.max(np.abs(y)), "rotating twice must give back x"
+    ry = rotate_groups(y).reshape(4, 3, 256)
+    assert np.allclose(np.linalg.norm(ry, axis=2), np.linalg.norm(y.reshape(4, 3, 256), axis=2), rtol=1e-13)
+
+
+def check_product_invariance(rotate_groups, seed=12):
+    """Rotating both operands leaves the fp64 product unchanged (1e-12 rel)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((16, 1024))
+    w = rng.standard_normal((24, 1024))
+    x[:, 7] *= 30.0
+    w[:, 300] *= 20.0
+    ref = x @ w.T
+    got = rotate_groups(x) @ rotate_groups(w).T
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel < 1e-12, f"rotated product differs: {rel}"
+
+
+# ------------------------------------------------------------------ bf16 round
+def check_bf16(bf16_round):
+    import torch
+    with open(os.path.join(GOLDEN, "bf16_values.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            v, _bits, want = line.split()
+            got = bf16_round(np.array([float(v)]))[0]
+            assert got == float(want), f"bf16({v}) = {got}, want {want}"
+    # Agrees with torch's fp32 -> bf16 conversion (nearest, ties to even) on
+    # values that are exact in fp32, ties included.
+    rng = np.random.default_rng(13)
+    base = rng.standard_normal(20000).astype(np.float32)
+    bits = base.view(np.uint32)
+    ties = ((bits & ~np.uint32(0xFFFF)) | np.uint32(0x8000)).view(np.float32)
+    vals = np.concatenate([base, ties, base * np.float32(1e-30), base * np.float32(1e30)])
+    ref = torch.from_numpy(vals).to(torch.bfloat16).double().numpy()
+    got = bf16_round(vals.astype(np.float64))
+    assert np.array_equal(got, ref), "bf16 rounding differs from torch on fp32-exact values"
+    big = np.array([3.3e38, 3.4e38, -3.5e38])
+    assert np.isinf(bf16_round(big)[2]) and np.isfinite(bf16_round(big)[0])
+
+
+# -------------------------------------------------------------- quantization
+def check_weight_int8(quantize_weights_int8, rotate_groups, seed=14):
+    rng = np.random.default_rng(seed)
+    w = (0.02 * rng.standard_normal((20, 768))).astype(np.float32)
+    w[:, [3, 400]] *= 20.0
+    w[5, :] = 0.0
+    q, s = quantize_weights_int8(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32 and q.shape == w.shape and s.shape == (20,)
+    wr = rotate_groups(w)
+    amax = np.max(np.abs(wr), axis=1)
+    # zero row
+    assert s[5] == 0.0 and np.all(q[5] == 0)
+    nz = np.arange(20) != 5
+    s64 = s.astype(np.float64)
+    # the scale is amax/127 rounded once to fp32
+    assert np.all(np.abs(s64[nz] - amax[nz] / 127.0) <= 2.0 ** -24 * amax[nz] / 127.0)
+    # every element within half a step of its source
+    err = np.abs(wr - q.astype(np.float64) * s64[:, None])
+    assert np.all(err[nz] <= 0.5 * s64[nz, None] * (1 + 1e-12)), "dequantized weight off by more than s/2"
+    # the amax element maps to +-127, and no code exceeds it
+    am = np.argmax(np.abs(wr), axis=1)
+    assert np.all(np.abs(q[nz, am[nz]]) == 127) and np.max(np.abs(q)) == 127
+    # signs agree
+    assert np.all((np.sign(q) == np.sign(wr)) | (q == 0))
+
+
+def check_weight_int4(quantize_weights_int4, unpack_int4, rotate_groups, seed=15):
+    rng = np.random.default_rng(seed)
+    w = (0.02 * rng.standard_normal((12, 768))).astype(np.float32)
+    w[:, [10, 600]] *= 20.0
+    w[2, 256:512] = 0.0
+    p, s = quantize_weights_int4(w)
+    assert p.dtype == np.uint8 and p.shape == (12, 384) and s.shape == (12, 3) and s.dtype == np.float32
+    q = unpack_int4(p).reshape(12, 3, 256)
+    wr = rotate_groups(w).reshape(12, 3, 256)
+    amax = np.max(np.abs(wr), axis=2)
+    assert s[2, 1] == 0.0 and np.all(q[2, 1] == 0)
+    s64 = s.astype(np.float64)
+    nz = s64 > 0
+    assert np.all(np.abs(s64[nz] - amax[nz] / 7.0) <= 2.0 ** -24 * amax[nz] / 7.0)
+    err = np.abs(wr - q * s64[:, :, None])
+    assert np.all(err[nz] <= 0.5 * s64[nz][:, None] * (1 + 1e-12)), "int4 dequant off by more than s/2"
+    am = np.argmax(np.abs(wr), axis=2)
+    qa = np.take_along_axis(np.abs(q), am[:, :, None], axis=2)[:, :, 0]
+    assert np.all(qa[nz] == 7) and np.max(np.abs(q)) == 7
+    assert np.all((np.sign(q) == np.sign(wr)) | (q == 0))
+
+
+def _planted(rng, rows, k, qmax, per_group):
+    """Integer matrix with |v| <= qmax and the extreme value hit in every row
+    (or every 256-group), plus power-of-two multipliers."""
+    v = rng.integers(-qmax, qmax + 1, size=(rows, k))
+    if per_group:
+        for g in range(k // 256):
+            v[:, 256 * g + rng.integers(0, 256)] = qmax * rng.choice([-1, 1], size=rows)
+        c = 2.0 ** rng.integers(-12, 3, size=(rows, k // 256))
+    else:
+        v[np.arange(rows), rng.integers(0, k, size=rows)] = qmax * rng.choice([-1, 1], size=rows)
+        c = 2.0 ** rng.integers(-12, 3, size=rows)
+    return v, c
+
+
+def check_planted_int8(quantize_weights_int8, hadamard_matrix, seed=16):
+    """W = W' . Q with integer W' (amax 127 c, c a power of two): then the
+    quantizer must return exactly q = W' and s = c."""
+    rng = np.random.default_rng(seed)
+    Q = hadamard_matrix(256) / 16.0
+    v, c = _planted(rng, 9, 512, 127, per_group=False)
+    wprime = v * c[:, None]
+    w = np.concatenate([wprime[:, :256] @ Q, wprime[:, 256:] @ Q], axis=1)
+    q, s = quantize_weights_int8(w)
+    assert np.array_equal(q.astype(np.int64), v), "planted codes not recovered"
+    assert np.array_equal(s.astype(np.float64), c), "planted scales not recovered"
+
+
+def check_planted_int4(quantize_weights_int4, unpack_int4, hadamard_matrix, seed=17):
+    rng = np.random.default_rng(seed)
+    Q = hadamard_matrix(256) / 16.0
+    v, c = _planted(rng, 7, 768, 7, per_group=True)
+    wprime = v * np.repeat(c, 256, axis=1)
+    w = np.concatenate([wprime[:, 256 * g:256 * (g + 1)] @ Q for g in range(3)], axis=1)
+    p, s = quantize_weights_int4(w)
+    assert np.array_equal(unpack_int4(p), v), "planted int4 codes not recovered"
+    assert np.array_equal(s.astype(np.float64), c), "planted int4 scales not recovered"
+
+
+def check_pack(pack_int4, unpack_int4):
+    """Two's-complement nibbles, even column in the low nibble."""
+    table = {(-1, 0): 0x0F, (0, -1): 0xF0, (7, -7): 0x97, (-7, 7): 0x79, (1, 2): 0x21, (-8, 0): 0x08, (3, -4): 0xC3}
+    for (a, b), byte in table.items():
+        got = pack_int4(np.array([[a, b]]))
+        assert got.dtype == np.uint8 and got[0, 0] == byte, f"pack({a},{b}) = {got[0, 0]:#x}, want {byte:#x}"
+    pairs = np.array([(a, b) for a in range(-7, 8) for b in range(-7, 8)])
+    assert len(pairs) == 225
+    codes = pairs.reshape(1, -1)
+    assert np.array_equal(unpack_int4(pack_int4(codes)), codes)
+
+
+# -------------------------------------------------------------------- products
+def check_int_accumulate(int_accumulate, seed=18):
+    rng = np.random.default_rng(seed)
+    a = rng.integers(-127, 128, size=(5, 512))
+    b = rng.integers(-127, 128, size=(4, 512))
+    got = int_accumulate(a.astype(np.int8), b.astype(np.int8))
+    for i in range(5):
+        for j in range(4):
+            assert got[i, j] == sum(int(a[i, t]) * int(b[j, t]) for t in range(512))
+    k = 12288
+    full = np.full((2, k), 127, dtype=np.int8)
+    neg = np.full((3, k), -127, dtype=np.int8)
+    got = int_accumulate(full, neg)
+    assert np.all(got == -127 * 127 * k) and got.dtype == np.int64
+
+
+def check_products_bruteforce(qgemm_w8, qgemm_w4, qgemm_w8a8, rotate_groups, bf16_round,
+                              quantize_weights_int8, quantize_weights_int4, unpack_int4, seed=19):
+    """Pure-Python loops over the quantized operands on tiny shapes."""
+    rng = np.random.default_rng(seed)
+    for m, n, k in ((3, 5, 256), (6, 4, 512)):
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        x[:, 2] *= 30.0
+        w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+        xr = rotate_groups(x)
+        xb = bf16_round(xr)
+        q8, s8 = quantize_weights_int8(w)
+        y8 = qgemm_w8(x, q8, s8)
+        p4, s4 = quantize_weights_int4(w)
+        q4 = unpack_int4(p4)
+        y4 = qgemm_w4(x, p4, s4)
+        y, acc, qa, sa = qgemm_w8a8(x, q8, s8)
+        amax = np.max(np.abs(xr), axis=1)
+        for i in range(m):
+            sai = float(np.float32(amax[i] / 127.0))
+            assert float(sa[i]) == sai
+            for t in range(k):
+                want = 0 if sai == 0 else int(max(-127, min(127, np.rint(xr[i, t] / sai))))
+                assert int(qa[i, t]) == want
+            for j in range(n):
+                ref8 = sum(float(xb[i, t]) * int(q8[j, t]) for t in range(k)) * float(s8[j])
+                ref4 = sum(float(xb[i, t]) * int(q4[j, t]) * float(s4[j, t // 256]) for t in range(k))
+                refacc = sum(int(qa[i, t]) * int(q8[j, t]) for t in range(k))
+                assert abs(y8[i, j] - ref8) <= 1e-12 * max(1.0, abs(ref8)), "w8 product"
+                assert abs(y4[i, j] - ref4) <= 1e-12 * max(1.0, abs(ref4)), "w4 product"
+                assert acc[i, j] == refacc, "w8a8 accumulator"
+                refy = refacc * float(sa[i]) * float(s8[j])
+                assert abs(y[i, j] - refy) <= 1e-15 * max(1e-30, abs(refy)) + 1e-300, "w8a8 output"
+
+
+def check_planted_w8a8(qgemm_w8a8, hadamard_matrix, seed=20):
+    """Integer X', W' with power-of-two row scales, X = X'.Q and W = W'.Q:
+    qa = X', sa = c_m, acc = X' W'^T exactly, y = acc c_m c_n exactly."""
+    rng = np.random.default_rng(seed)
+    Q = hadamard_matrix(256) / 16.0
+    xv, xc = _planted(rng, 6, 512, 127, per_group=False)
+    wv, wc = _planted(rng, 5, 512, 127, per_group=False)
+    rot = lambda a: np.concatenate([a[:, :256] @ Q, a[:, 256:] @ Q], axis=1)
+    x = rot(xv * xc[:, None])
+    w_codes = wv.astype(np.int8)
+    y, acc, qa, sa = qgemm_w8a8(x, w_codes, wc.astype(np.float32))
+    assert np.array_equal(qa.astype(np.int64), xv), "planted activation codes"
+    assert np.array_equal(sa.astype(np.float64), xc), "planted activation scales"
+    ref = np.array([[sum(int(xv[i, t]) * int(wv[j, t]) for t in range(512)) for j in range(5)] for i in range(6)])
+    assert np.array_equal(acc, ref), "planted accumulator"
+    assert np.array_equal(y, ref * xc[:, None] * wc[None, :]), "planted output"
+
+
+def check_rotation_helps(quantize_weights_int8, dequantize_int8, rotate_groups, seed=21):
+    """Sanity of the method's purpose (not parity): with outlier input columns,
+    rotating before per-row int8 lowers the weight error measured in the
+    original basis (the dequantized rotated weight is rotated back)."""
+    rng = np.random.default_rng(seed)
+    w = (0.02 * rng.standard_normal((64, 1024))).astype(np.float32)
+    w[:, rng.choice(1024, 5, replace=False)] *= 20.0
+    q, s = quantize_weights_int8(w)
+    back = rotate_groups(dequantize_int8(q, s))
+    err_rot = np.linalg.norm(back - w) / np.linalg.norm(w)
+    s0 = np.max(np.abs(w), axis=1) / 127.0
+    plain = np.clip(np.rint(w / s0[:, None]), -127, 127) * s0[:, None]
+    err_plain = np.linalg.norm(plain - w) / np.linalg.norm(w)
+    assert err_rot < 0.5 * err_plain, (err_rot, err_plain)

@@ -1,0 +1,130 @@
+"""Planted-fault controls: each pin must turn red on a deliberately broken copy
+of an oracle function. The faults are planted here, in CPU-only copies of the
+oracle's arithmetic; nothing touches a GPU."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import quantize as oq
+from tests import pins
+
+
+def _walsh_ordered(n=256):
+    """Hadamard rows sorted by number of sign changes (sequency order)."""
+    h = oracle.hadamard_matrix(n)
+    changes = np.sum(h[:, 1:] != h[:, :-1], axis=1)
+    return h[np.argsort(changes)][:, np.argsort(changes)]
+
+
+def _rotate_with(hmat, scale=1.0 / 16.0):
+    def rot(x):
+        x = np.asarray(x, dtype=np.float64)
+        r, k = x.shape
+        return np.matmul(x.reshape(r, k // 256, 256), hmat * scale).reshape(r, k)
+    return rot
+
+
+def test_walsh_ordering_caught():
+    with pytest.raises(AssertionError):
+        pins.check_hadamard(_walsh_ordered)
+
+
+def test_missing_normalization_caught():
+    with pytest.raises(AssertionError):
+        pins.check_rotation(_rotate_with(oracle.hadamard_matrix(256), 1.0), oracle.hadamard_matrix)
+
+
+def test_double_normalization_caught():
+    with pytest.raises(AssertionError):
+        pins.check_product_invariance(_rotate_with(oracle.hadamard_matrix(256), 1.0 / 256.0))
+
+
+def test_rotation_across_groups_caught():
+    def rot_full(x):
+        x = np.asarray(x, dtype=np.float64)
+        k = x.shape[1]
+        return x @ (oracle.hadamard_matrix(k) / np.sqrt(k))
+    with pytest.raises(AssertionError):
+        pins.check_rotation(rot_full, oracle.hadamard_matrix)
+
+
+def test_swapped_nibbles_caught():
+    def pack_swapped(q):
+        q = np.asarray(q, dtype=np.int64)
+        return ((q[..., 1::2] & 0xF) | ((q[..., 0::2] & 0xF) << 4)).astype(np.uint8)
+    with pytest.raises(AssertionError):
+        pins.check_pack(pack_swapped, oracle.unpack_int4)
+
+
+def test_wrong_qmax_caught():
+    def q8_128(w):
+        wr = oracle.rotate_groups(w)
+        s = (np.max(np.abs(wr), axis=1) / 128.0).astype(np.float32)
+        return oq._codes(wr, s[:, None], 127).astype(np.int8), s
+    with pytest.raises(AssertionError):
+        pins.check_weight_int8(q8_128, oracle.rotate_groups)
+
+
+def test_truncating_codes_caught():
+    def q8_trunc(w):
+        wr = oracle.rotate_groups(w)
+        s = (np.max(np.abs(wr), axis=1) / 127.0).astype(np.float32)
+        q = np.where(s[:, None] > 0, np.trunc(wr / np.maximum(s[:, None], 1e-38)), 0)
+        return np.clip(q, -127, 127).astype(np.int8), s
+    with pytest.raises(AssertionError):
+        pins.check_weight_int8(q8_trunc, oracle.rotate_groups)
+
+
+def test_int4_range_8_caught():
+    def q4_8(w):
+        wr = oracle.rotate_groups(w)
+        n, k = wr.shape
+        g = wr.reshape(n, k // 256, 256)
+        s = (np.max(np.abs(g), axis=2) / 8.0).astype(np.float32)
+        return oracle.pack_int4(oq._codes(g, s[:, :, None], 8).reshape(n, k)), s
+    with pytest.raises(AssertionError):
+        pins.check_weight_int4(q4_8, oracle.unpack_int4, oracle.rotate_groups)
+
+
+def test_truncating_bf16_caught():
+    def bf16_trunc(x):
+        x32 = np.asarray(x, dtype=np.float32)
+        return (x32.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+    with pytest.raises(AssertionError):
+        pins.check_bf16(bf16_trunc)
+
+
+def test_w4_scale_index_caught():
+    def w4_tiled(x, packed, s, rotate=True):
+        xb = oracle.bf16_round(oracle.rotate_groups(x))
+        q = oracle.unpack_int4(packed).astype(np.float64)
+        return xb @ (q * np.tile(np.asarray(s, np.float64), (1, 256))).T
+    with pytest.raises(AssertionError):
+        pins.check_products_bruteforce(
+            oracle.qgemm_w8, w4_tiled, oracle.qgemm_w8a8, oracle.rotate_groups, oracle.bf16_round,
+            oracle.quantize_weights_int8, oracle.quantize_weights_int4, oracle.unpack_int4)
+
+
+def test_w8_missing_bf16_caught():
+    def w8_no_bf16(x, q, s, rotate=True):
+        return oracle.rotate_groups(x) @ oracle.dequantize_int8(q, s).T
+    with pytest.raises(AssertionError):
+        pins.check_products_bruteforce(
+            w8_no_bf16, oracle.qgemm_w4, oracle.qgemm_w8a8, oracle.rotate_groups, oracle.bf16_round,
+            oracle.quantize_weights_int8, oracle.quantize_weights_int4, oracle.unpack_int4)
+
+
+def test_w8a8_dropped_weight_scale_caught():
+    def w8a8_no_sw(x, q, sw, rotate=True):
+        y, acc, qa, sa = oracle.qgemm_w8a8(x, q, sw, rotate)
+        return acc * sa.astype(np.float64)[:, None], acc, qa, sa
+    with pytest.raises(AssertionError):
+        pins.check_planted_w8a8(w8a8_no_sw, oracle.hadamard_matrix)
+
+
+def test_w8a8_unrotated_activations_caught():
+    def w8a8_no_rot(x, q, sw, rotate=True):
+        return oracle.qgemm_w8a8(x, q, sw, rotate=False)
+    with pytest.raises(AssertionError):
+        pins.check_planted_w8a8(w8a8_no_rot, oracle.hadamard_matrix)
