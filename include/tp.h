@@ -1,0 +1,228 @@
+/*
+ * tp.h -- rotated, quantized linear projections ("ConvRot") for AMD Instinct
+ * MI355X (gfx950). C ABI: plain device pointers, sizes and a HIP stream.
+ *
+ * The method (tensai docs, "画像生成" (image generation), section "幅とメモリ"
+ * (width and memory)): every weight matrix is rotated by a 256x256 Hadamard
+ * matrix on each 256-wide group of input columns and then quantized (8-bit per
+ * row by default, 4-bit optionally); each activation row gets the same
+ * rotation on the device before the product, one product with H per 256-group,
+ * so that, H being orthogonal, the product equals the float one up to
+ * quantization error while outlier columns no longer dominate a row's scale.
+ * Section "GPU" of the same page: the device quantizes each product's
+ * activations (per token here, for the int8 x int8 product).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Rotation    Q = H / 16 with H the Sylvester Hadamard matrix of order 256 in
+ *             natural order, H[i][j] = (-1)^popcount(i & j). Q is orthonormal
+ *             and symmetric. A row x of length K is rotated group by group:
+ *             x'[256g + j] = sum_i x[256g + i] * Q[i][j].
+ * Shapes      Matrices are row-major with an explicit leading dimension (ld, in
+ *             ELEMENTS of the stated type, except packed int4 whose ld is in
+ *             bytes). Activations A are [m, k]; weights W are [n, k] (output
+ *             rows by input columns); outputs C are [m, n]. k must be a
+ *             positive multiple of 256. m == 0 or n == 0 is a valid no-op.
+ * Pointers    All data pointers are DEVICE pointers owned by the caller. The
+ *             library keeps no pointer after a call returns and allocates no
+ *             memory: scratch comes from the caller's workspace, sized with
+ *             tp_workspace_size(). Base pointers must be 16-byte aligned and
+ *             every row pitch (ld * element size) a multiple of 16 bytes;
+ *             scale arrays must be 4-byte aligned.
+ * Streams     Work is enqueued on `stream` (NULL = the default stream) and runs
+ *             asynchronously; no call synchronizes or copies to the host.
+ *             Calls that overlap on different streams and share buffers race.
+ * Errors      Every argument is validated BEFORE any HIP call, so a refused
+ *             call has enqueued nothing. A HIP launch failure returns
+ *             TP_ERR_HIP. The calling thread's last error message is available
+ *             from tp_last_error_message().
+ * Results     Deterministic: the same inputs give the same output bytes (no
+ *             atomics, fixed reduction orders).
+ */
+#ifndef TP_H_
+#define TP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TP_ABI_VERSION 1
+
+typedef enum tp_status {
+  TP_OK = 0,
+  TP_ERR_NULL_POINTER = 1,          /* a required pointer is NULL              */
+  TP_ERR_BAD_SHAPE = 2,             /* negative size, or k <= 0                */
+  TP_ERR_K_NOT_MULTIPLE_OF_256 = 3, /* a group would straddle the row end      */
+  TP_ERR_BAD_LEADING_DIM = 4,       /* ld smaller than the row length          */
+  TP_ERR_MISALIGNED = 5,            /* pointer or row pitch not 16-B aligned   */
+  TP_ERR_UNSUPPORTED_DTYPE = 6,     /* dtype code not allowed for this operand */
+  TP_ERR_UNSUPPORTED_BITS = 7,      /* bits is neither 8 nor 4                 */
+  TP_ERR_SIZE_OVERFLOW = 8,         /* a byte size overflows int64             */
+  TP_ERR_WORKSPACE_TOO_SMALL = 9,   /* workspace NULL or below the query       */
+  TP_ERR_BAD_ALIASING = 10,         /* partially overlapping in/out buffers    */
+  TP_ERR_BAD_FLAGS = 11,            /* unknown a_flags value                   */
+  TP_ERR_HIP = 12                   /* a HIP runtime call or launch failed     */
+} tp_status;
+
+/* Element types of floating-point operands. */
+typedef enum tp_dtype {
+  TP_F32 = 0,  /* IEEE binary32                                   */
+  TP_BF16 = 1  /* bfloat16 (top half of a binary32), RNE on store */
+} tp_dtype;
+
+/* a_flags of the products: what the activation operand already is. */
+#define TP_A_PREROTATED 0 /* A already holds rotated rows (x . blockdiag(Q)) */
+#define TP_A_ROTATE 1     /* A holds plain rows; the library rotates them    */
+
+/* Operation codes for tp_workspace_size(). */
+typedef enum tp_op {
+  TP_OP_QGEMM_W8 = 1,
+  TP_OP_QGEMM_W4 = 2,
+  TP_OP_QGEMM_W8A8 = 3
+} tp_op;
+
+/*
+ * tp_rotate_quantize_weights -- offline rotate-and-quantize of a weight
+ * matrix (tensai docs, "画像生成", section "幅とメモリ": quantize while loading,
+ * 8-bit by default or 4-bit, after rotating per 256 input columns; section
+ * "チェックポイントの入手": per-row scaled int8 after the rotation).
+ *
+ *   w       [n, k] weights, dtype w_dtype (TP_F32 or TP_BF16), row pitch ldw
+ *           elements.
+ *   bits    8: q is int8 [n, k] (row pitch ldq bytes), scales is fp32 [n]:
+ *              scales[r] = fp32(max_j |W'[r, j]| / 127) (fp64 divide, one
+ *              rounding), q = clamp(rint(W' / scales[r]), -127, 127).
+ *           4: q is packed int4 [n, k/2] bytes (row pitch ldq bytes): byte j of
+ *              a row holds the code of column 2j in its low nibble and of
+ *              column 2j+1 in its high nibble, two's complement, codes in
+ *              [-7, 7]; scales is fp32 [n, k/256] (contiguous):
+ *              scales[r, g] = fp32(max |W'| over group g of row r / 7).
+ *   The rotation W' = W . blockdiag(Q) is computed in fp64 and the codes use
+ *   round-half-to-even of W' / (double)scale. A row (or group) of zeros gets
+ *   scale 0 and codes 0. w and q/scales must not overlap.
+ */
+tp_status tp_rotate_quantize_weights(const void* w, tp_dtype w_dtype, int64_t n, int64_t k,
+                                     int64_t ldw, int bits, void* q, int64_t ldq,
+                                     float* scales, hipStream_t stream);
+
+/*
+ * tp_hadamard_rotate_rows -- activation rotation y = x . blockdiag(Q)
+ * (tensai docs, "画像生成", section "幅とメモリ": the product's input gets the
+ * same rotation, rows taken as 256-groups, one product with H).
+ *
+ *   x       [m, k], dtype x_dtype (TP_F32 or TP_BF16), row pitch ldx.
+ *   y       [m, k], dtype y_dtype (TP_F32 or TP_BF16), row pitch ldy.
+ *   Arithmetic is fp32 (a fast Walsh-Hadamard transform per group); a bf16
+ *   output is rounded to nearest even once. In place (y == x) is allowed when
+ *   the dtypes and leading dimensions match; any other overlap is refused.
+ */
+tp_status tp_hadamard_rotate_rows(const void* x, tp_dtype x_dtype, int64_t m, int64_t k,
+                                  int64_t ldx, void* y, tp_dtype y_dtype, int64_t ldy,
+                                  hipStream_t stream);
+
+/*
+ * tp_quantize_rows_int8 -- rotate (unless a_flags == TP_A_PREROTATED) and
+ * quantize activations per row for the int8 x int8 product (tensai docs,
+ * "画像生成", section "GPU": each product's activations are quantized on the
+ * device).
+ *
+ *   x       [m, k], TP_F32 or TP_BF16, row pitch ldx.
+ *   qa      int8 [m, k], row pitch ldqa bytes.
+ *   sa      fp32 [m]: sa[r] = fp32(max_j |X'[r, j]| / 127).
+ *   Codes are clamp(rint(X' / (double)sa[r]), -127, 127), 0 for a zero row.
+ *   The rotation is exact fp64 arithmetic, so the codes match an fp64
+ *   reference bit for bit.
+ */
+tp_status tp_quantize_rows_int8(const void* x, tp_dtype x_dtype, int64_t m, int64_t k,
+                                int64_t ldx, int a_flags, int8_t* qa, int64_t ldqa, float* sa,
+                                hipStream_t stream);
+
+/*
+ * tp_workspace_size -- bytes of device workspace the product `op` needs for
+ * these sizes and a_flags (0 when none is needed). Returns 0 for invalid
+ * sizes as well; the product call itself reports the error.
+ */
+size_t tp_workspace_size(tp_op op, int64_t m, int64_t n, int64_t k, int a_flags);
+
+/*
+ * tp_qgemm_w8 -- weight-only int8 product (tensai docs, "画像生成", section
+ * "幅とメモリ" for the format; the bf16 matrix-unit arithmetic with fp32 sums
+ * is the precision the TensorFold pull request #948 describes for its
+ * projections).
+ *
+ *   C[r, c] = s[c] * sum_j bf16(A'[r, j]) * q[c, j]
+ *
+ *   a        [m, k] activations, row pitch lda. With TP_A_ROTATE, a is TP_F32
+ *            or TP_BF16 and is rotated (fp32 arithmetic) and rounded to bf16
+ *            into the workspace first. With TP_A_PREROTATED, a must be TP_BF16
+ *            and already rotated.
+ *   q        int8 [n, k] codes, row pitch ldq bytes; w_scales fp32 [n].
+ *   c        [m, n], c_dtype TP_F32 or TP_BF16 (RNE), row pitch ldc.
+ *   The product runs on bf16 MFMA with fp32 accumulation; the scale is
+ *   applied in fp32 in the epilogue. c must not overlap any input.
+ */
+tp_status tp_qgemm_w8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags,
+                      const int8_t* q, int64_t ldq, const float* w_scales, int64_t m, int64_t n,
+                      int64_t k, void* c, tp_dtype c_dtype, int64_t ldc, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tp_qgemm_w4 -- weight-only int4 product, one scale per (row, 256-group)
+ * (tensai docs, "画像生成", section "幅とメモリ": the 4-bit width "-q4";
+ * TensorPencil README: the "INT4 ConvRot" format).
+ *
+ *   C[r, c] = sum_g s[c, g] * sum_{j in group g} bf16(A'[r, j]) * q[c, j]
+ *
+ *   q        packed int4 [n, k/2] bytes (layout as tp_rotate_quantize_weights
+ *            with bits = 4), row pitch ldq bytes; w_scales fp32 [n, k/256].
+ *   Other arguments as tp_qgemm_w8. Each group's partial sum is kept in fp32
+ *   and folded with its scale at the group boundary.
+ */
+tp_status tp_qgemm_w4(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags,
+                      const uint8_t* q, int64_t ldq, const float* w_scales, int64_t m, int64_t n,
+                      int64_t k, void* c, tp_dtype c_dtype, int64_t ldc, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tp_qgemm_w8a8 -- int8 x int8 product with per-token activation
+ * quantization (tensai docs, "画像生成", section "GPU").
+ *
+ *   acc[r, c] = sum_j qa[r, j] * q[c, j]        (exact, int32)
+ *   C[r, c]   = (float(acc[r, c]) * sa[r]) * sw[c]   (fp32, then c_dtype)
+ *
+ *   a        [m, k] activations (TP_F32 or TP_BF16), row pitch lda; rotated
+ *            first unless a_flags == TP_A_PREROTATED; then quantized exactly as
+ *            tp_quantize_rows_int8.
+ *   q        int8 [n, k] weight codes, row pitch ldq; w_scales fp32 [n].
+ *   c        [m, n], TP_F32 or TP_BF16, row pitch ldc.
+ *   qa_out   optional int8 [m, k] (pitch k bytes) and sa_out optional fp32
+ *            [m]: when both are given the activation codes and scales are
+ *            written there (and the workspace is not needed for them).
+ *   acc_out  optional int32 [m, n], row pitch ld_acc: the raw accumulators.
+ *   k * 127 * 127 must fit in int32 (k <= 133144).
+ */
+tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags,
+                        const int8_t* q, int64_t ldq, const float* w_scales, int64_t m,
+                        int64_t n, int64_t k, void* c, tp_dtype c_dtype, int64_t ldc,
+                        int8_t* qa_out, float* sa_out, int32_t* acc_out, int64_t ld_acc,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* tp_status_string(tp_status status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* tp_last_error_message(void);
+
+/* TP_ABI_VERSION of the loaded library. */
+int tp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_H_ */

@@ -1,0 +1,178 @@
+"""Rotated, quantized linear projections ("ConvRot") on AMD Instinct MI355X.
+
+Thin Python binding of libtp.so (C ABI in include/tp.h). Each function has the
+name of the C entry point it calls and only marshals arguments: it takes
+device tensors, allocates outputs (and the workspace, unless one is given)
+with PyTorch, and passes data pointers and the current HIP stream. Every step
+of the computation runs in the library's HIP kernels; there is no CPU path.
+
+    tp_rotate_quantize_weights(w, bits)        -> (q, scales)
+    tp_hadamard_rotate_rows(x, out_dtype)      -> y = x . blockdiag(H/16)
+    tp_quantize_rows_int8(x, rotate)           -> (qa, sa)
+    tp_qgemm_w8(a, q, s, rotate, out_dtype)    -> C
+    tp_qgemm_w4(a, q, s, rotate, out_dtype)    -> C
+    tp_qgemm_w8a8(a, q, s, rotate, out_dtype, want_codes, want_acc)
+                                               -> C (and qa, sa, acc on request)
+"""
+
+import torch
+
+from . import _lib
+from ._lib import TPError, TP_A_PREROTATED, TP_A_ROTATE  # noqa: F401
+
+_DTYPE = {torch.float32: _lib.TP_F32, torch.bfloat16: _lib.TP_BF16}
+
+
+def _dt(t):
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)") from None
+
+
+def _mat(t, name):
+    """Check a 2-D row-major CUDA tensor; return its row pitch in elements."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last dimension")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _vec(t, name, numel):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != numel:
+        raise ValueError(f"{name} must be a contiguous float32 tensor with {numel} elements")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def tp_workspace_size(op, m, n, k, a_flags):
+    return int(_lib.load().tp_workspace_size(op, m, n, k, a_flags))
+
+
+def tp_rotate_quantize_weights(w, bits=8, q=None, scales=None, stream=None):
+    """Rotate W [n, k] per 256-group (fp64) and quantize: bits=8 gives int8
+    [n, k] and fp32 [n] scales; bits=4 gives packed uint8 [n, k/2] and fp32
+    [n, k/256] scales."""
+    ldw = _mat(w, "w")
+    n, k = w.shape
+    if q is None:
+        q = torch.empty((n, k if bits == 8 else k // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
+                        device=w.device)
+    if scales is None:
+        scales = torch.empty((n,) if bits == 8 else (n, max(k // 256, 0)), dtype=torch.float32, device=w.device)
+    ldq = _mat(q, "q")
+    _vec(scales, "scales", n * (1 if bits == 8 else k // 256))
+    _lib.check(_lib.load().tp_rotate_quantize_weights(w.data_ptr(), _dt(w), n, k, ldw, bits, q.data_ptr(), ldq,
+                                                      scales.data_ptr(), _stream(stream)))
+    return q, scales
+
+
+def tp_hadamard_rotate_rows(x, out_dtype=None, out=None, stream=None):
+    """y = x . blockdiag(H/16) in fp32 arithmetic; out may be x (in place)."""
+    ldx = _mat(x, "x")
+    m, k = x.shape
+    if out is None:
+        out = torch.empty((m, k), dtype=out_dtype or x.dtype, device=x.device)
+    ldy = _mat(out, "out")
+    _lib.check(_lib.load().tp_hadamard_rotate_rows(x.data_ptr(), _dt(x), m, k, ldx, out.data_ptr(), _dt(out), ldy,
+                                                   _stream(stream)))
+    return out
+
+
+def tp_quantize_rows_int8(x, rotate=True, qa=None, sa=None, stream=None):
+    """Rotate (unless rotate=False) and quantize each row to int8 with one fp32
+    scale per row."""
+    ldx = _mat(x, "x")
+    m, k = x.shape
+    if qa is None:
+        qa = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if sa is None:
+        sa = torch.empty((m,), dtype=torch.float32, device=x.device)
+    ldqa = _mat(qa, "qa")
+    _vec(sa, "sa", m)
+    flags = TP_A_ROTATE if rotate else TP_A_PREROTATED
+    _lib.check(_lib.load().tp_quantize_rows_int8(x.data_ptr(), _dt(x), m, k, ldx, flags, qa.data_ptr(), ldqa,
+                                                 sa.data_ptr(), _stream(stream)))
+    return qa, sa
+
+
+def _workspace(op, m, n, k, flags, device, workspace):
+    need = tp_workspace_size(op, m, n, k, flags)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _weight_only(fn_name, op, a, q, scales, rotate, out_dtype, out, workspace, stream, bits):
+    lda = _mat(a, "a")
+    m, k = a.shape
+    n = q.shape[0]
+    ldq = _mat(q, "q")
+    _vec(scales, "w_scales", n * (1 if bits == 8 else k // 256))
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    ldc = _mat(out, "out")
+    flags = TP_A_ROTATE if rotate else TP_A_PREROTATED
+    ws, ws_bytes = _workspace(op, m, n, k, flags, a.device, workspace)
+    fn = getattr(_lib.load(), fn_name)
+    _lib.check(fn(a.data_ptr(), _dt(a), lda, flags, q.data_ptr(), ldq, scales.data_ptr(), m, n, k, out.data_ptr(),
+                  _dt(out), ldc, ws.data_ptr(), ws_bytes, _stream(stream)))
+    return out
+
+
+def tp_qgemm_w8(a, q, scales, rotate=True, out_dtype=torch.bfloat16, out=None, workspace=None, stream=None):
+    """C = (bf16(A') . q^T) * s[n]; A' = rotated a (or a itself if rotate=False,
+    which must then be bf16)."""
+    return _weight_only("tp_qgemm_w8", _lib.TP_OP_QGEMM_W8, a, q, scales, rotate, out_dtype, out, workspace,
+                        stream, 8)
+
+
+def tp_qgemm_w4(a, q, scales, rotate=True, out_dtype=torch.bfloat16, out=None, workspace=None, stream=None):
+    """C = sum_g s[n, g] (bf16(A'_g) . q_g^T) with packed int4 q [n, k/2]."""
+    return _weight_only("tp_qgemm_w4", _lib.TP_OP_QGEMM_W4, a, q, scales, rotate, out_dtype, out, workspace,
+                        stream, 4)
+
+
+def tp_qgemm_w8a8(a, q, scales, rotate=True, out_dtype=torch.float32, out=None, want_codes=False, want_acc=False,
+                  workspace=None, stream=None):
+    """Per-token int8 activations x int8 weights; int32 sums; fp32 epilogue
+    (float(acc) * sa[m]) * sw[n]. Returns C, or (C, qa, sa, acc) with the
+    requested intermediates (None where not requested)."""
+    lda = _mat(a, "a")
+    m, k = a.shape
+    n = q.shape[0]
+    ldq = _mat(q, "q")
+    _vec(scales, "w_scales", n)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    ldc = _mat(out, "out")
+    qa = sa = acc = None
+    if want_codes:
+        qa = torch.empty((m, k), dtype=torch.int8, device=a.device)
+        sa = torch.empty((m,), dtype=torch.float32, device=a.device)
+    if want_acc:
+        acc = torch.empty((m, n), dtype=torch.int32, device=a.device)
+    flags = TP_A_ROTATE if rotate else TP_A_PREROTATED
+    if want_codes:
+        ws, ws_bytes = (None, 0) if workspace is None else (workspace, workspace.numel() * workspace.element_size())
+    else:
+        ws, ws_bytes = _workspace(_lib.TP_OP_QGEMM_W8A8, m, n, k, flags, a.device, workspace)
+    ld_acc = _mat(acc, "acc") if acc is not None else 0
+    _lib.check(_lib.load().tp_qgemm_w8a8(a.data_ptr(), _dt(a), lda, flags, q.data_ptr(), ldq, scales.data_ptr(), m, n,
+                                         k, out.data_ptr(), _dt(out), ldc, _ptr(qa), _ptr(sa), _ptr(acc), ld_acc,
+                                         _ptr(ws), ws_bytes, _stream(stream)))
+    if want_codes or want_acc:
+        return out, qa, sa, acc
+    return out

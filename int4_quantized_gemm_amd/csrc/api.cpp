@@ -1,0 +1,360 @@
+// C ABI of the rotated, quantized projection library (declared in
+// include/tp.h). Every argument is validated here before any HIP call, so a
+// refused call has enqueued no work (the TensorFold pull request #948 review
+// asks for sizes and products to be checked before any device work; kvad-gpu
+// internals, "Quantised weights on the GPU", refuses dimensions not divisible
+// by 256 up front rather than failing halfway).
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/tp.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+tp_status fail(tp_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tp_status fail(tp_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+tp_status ok() {
+  g_msg[0] = '\0';
+  return TP_OK;
+}
+
+tp_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_add_overflow(a, b, out); }
+
+// Byte extent [p, p + bytes) of a row-major matrix: (rows-1)*pitch + row_bytes.
+struct Extent {
+  uintptr_t lo = 0, hi = 0;
+};
+
+Extent extent_of(const void* p, int64_t rows, int64_t pitch_bytes, int64_t row_bytes) {
+  Extent e;
+  e.lo = (uintptr_t)p;
+  e.hi = rows > 0 ? e.lo + (uintptr_t)((rows - 1) * pitch_bytes + row_bytes) : e.lo;
+  return e;
+}
+
+bool overlaps(const Extent& a, const Extent& b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+int64_t dtype_size(tp_dtype d) { return d == TP_BF16 ? 2 : 4; }
+bool dtype_ok(int d) { return d == TP_F32 || d == TP_BF16; }
+
+// Validate one row-major operand: non-null, ld >= row length, pitch and base
+// 16-byte aligned, total extent representable. On success stores the extent.
+tp_status check_matrix(const char* name, const void* p, int64_t rows, int64_t cols_bytes, int64_t ld,
+                       int64_t elem_bytes, Extent* ext) {
+  if (!p) return fail(TP_ERR_NULL_POINTER, "%s is NULL", name);
+  int64_t pitch;
+  if (!mul_ok(ld, elem_bytes, &pitch)) return fail(TP_ERR_SIZE_OVERFLOW, "%s: ld * element size overflows", name);
+  if (ld < 0 || pitch < cols_bytes)
+    return fail(TP_ERR_BAD_LEADING_DIM, "%s: leading dimension %lld is smaller than the row (%lld bytes)", name,
+                (long long)ld, (long long)cols_bytes);
+  int64_t span;
+  if (rows > 0) {
+    if (!mul_ok(rows - 1, pitch, &span) || !add_ok(span, cols_bytes, &span))
+      return fail(TP_ERR_SIZE_OVERFLOW, "%s: byte extent overflows", name);
+  }
+  if (((uintptr_t)p & 15u) != 0) return fail(TP_ERR_MISALIGNED, "%s: base pointer is not 16-byte aligned", name);
+  if (pitch % 16 != 0) return fail(TP_ERR_MISALIGNED, "%s: row pitch of %lld bytes is not a multiple of 16", name,
+                                   (long long)pitch);
+  *ext = extent_of(p, rows, pitch, cols_bytes);
+  return TP_OK;
+}
+
+tp_status check_vector(const char* name, const void* p, int64_t count, Extent* ext) {
+  if (!p) return fail(TP_ERR_NULL_POINTER, "%s is NULL", name);
+  if (((uintptr_t)p & 3u) != 0) return fail(TP_ERR_MISALIGNED, "%s: not 4-byte aligned", name);
+  int64_t bytes;
+  if (!mul_ok(count, 4, &bytes)) return fail(TP_ERR_SIZE_OVERFLOW, "%s: size overflows", name);
+  ext->lo = (uintptr_t)p;
+  ext->hi = ext->lo + (uintptr_t)bytes;
+  return TP_OK;
+}
+
+tp_status check_sizes(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0) return fail(TP_ERR_BAD_SHAPE, "negative size (m=%lld, n=%lld)", (long long)m, (long long)n);
+  if (k <= 0) return fail(TP_ERR_BAD_SHAPE, "k must be positive (k=%lld)", (long long)k);
+  if (k % 256 != 0)
+    return fail(TP_ERR_K_NOT_MULTIPLE_OF_256, "k=%lld is not a multiple of 256 (the rotation group)", (long long)k);
+  if (m > INT_MAX || n > INT_MAX || k > INT_MAX)
+    return fail(TP_ERR_BAD_SHAPE, "size above 2^31-1 (m=%lld, n=%lld, k=%lld)", (long long)m, (long long)n,
+                (long long)k);
+  return TP_OK;
+}
+
+#define TP_TRY(expr)                  \
+  do {                                \
+    tp_status _st = (expr);           \
+    if (_st != TP_OK) return _st;     \
+  } while (0)
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout: W8/W4 with TP_A_ROTATE: bf16 A' [m, k].
+// W8A8: int8 qa [m, k] then (256-byte aligned) fp32 sa [m].
+bool workspace_bytes_for(tp_op op, int64_t m, int64_t k, int a_flags, int64_t* out) {
+  int64_t mk;
+  if (!mul_ok(m, k, &mk)) return false;
+  if (op == TP_OP_QGEMM_W8 || op == TP_OP_QGEMM_W4) {
+    if (a_flags != TP_A_ROTATE) {
+      *out = 0;
+      return true;
+    }
+    return mul_ok(mk, 2, out);
+  }
+  if (op == TP_OP_QGEMM_W8A8) {
+    int64_t sa;
+    if (!mul_ok(m, 4, &sa)) return false;
+    if (mk > INT64_MAX - 512 - sa) return false;
+    *out = round_up(mk, 256) + sa;
+    return true;
+  }
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_status_string(tp_status s) {
+  switch (s) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_NULL_POINTER: return "TP_ERR_NULL_POINTER";
+    case TP_ERR_BAD_SHAPE: return "TP_ERR_BAD_SHAPE";
+    case TP_ERR_K_NOT_MULTIPLE_OF_256: return "TP_ERR_K_NOT_MULTIPLE_OF_256";
+    case TP_ERR_BAD_LEADING_DIM: return "TP_ERR_BAD_LEADING_DIM";
+    case TP_ERR_MISALIGNED: return "TP_ERR_MISALIGNED";
+    case TP_ERR_UNSUPPORTED_DTYPE: return "TP_ERR_UNSUPPORTED_DTYPE";
+    case TP_ERR_UNSUPPORTED_BITS: return "TP_ERR_UNSUPPORTED_BITS";
+    case TP_ERR_SIZE_OVERFLOW: return "TP_ERR_SIZE_OVERFLOW";
+    case TP_ERR_WORKSPACE_TOO_SMALL: return "TP_ERR_WORKSPACE_TOO_SMALL";
+    case TP_ERR_BAD_ALIASING: return "TP_ERR_BAD_ALIASING";
+    case TP_ERR_BAD_FLAGS: return "TP_ERR_BAD_FLAGS";
+    case TP_ERR_HIP: return "TP_ERR_HIP";
+  }
+  return "TP_ERR_UNKNOWN";
+}
+
+const char* tp_last_error_message(void) { return g_msg; }
+
+int tp_abi_version(void) { return TP_ABI_VERSION; }
+
+size_t tp_workspace_size(tp_op op, int64_t m, int64_t n, int64_t k, int a_flags) {
+  (void)n;
+  if (m < 0 || k <= 0) return 0;
+  int64_t b;
+  if (!workspace_bytes_for(op, m, k, a_flags, &b)) return 0;
+  return (size_t)b;
+}
+
+tp_status tp_rotate_quantize_weights(const void* w, tp_dtype w_dtype, int64_t n, int64_t k, int64_t ldw, int bits,
+                                     void* q, int64_t ldq, float* scales, hipStream_t stream) {
+  if (!dtype_ok(w_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "w_dtype %d is not TP_F32 or TP_BF16", (int)w_dtype);
+  if (bits != 8 && bits != 4) return fail(TP_ERR_UNSUPPORTED_BITS, "bits=%d (expected 8 or 4)", bits);
+  TP_TRY(check_sizes(0, n, k));
+  Extent ew, eq, es;
+  TP_TRY(check_matrix("w", w, n, k * dtype_size(w_dtype), ldw, dtype_size(w_dtype), &ew));
+  TP_TRY(check_matrix("q", q, n, bits == 8 ? k : k / 2, ldq, 1, &eq));
+  int64_t ns;
+  if (!mul_ok(n, bits == 8 ? 1 : k / 256, &ns)) return fail(TP_ERR_SIZE_OVERFLOW, "scale count overflows");
+  TP_TRY(check_vector("scales", scales, ns, &es));
+  if (overlaps(ew, eq) || overlaps(ew, es) || overlaps(eq, es))
+    return fail(TP_ERR_BAD_ALIASING, "w, q and scales must not overlap");
+  if (n == 0) return ok();
+  return hip_status(tp::launch_rotq_rows(w, w_dtype == TP_BF16, ldw, n, k, true, bits, q, ldq, scales, stream),
+                    "rotate-quantize launch");
+}
+
+tp_status tp_hadamard_rotate_rows(const void* x, tp_dtype x_dtype, int64_t m, int64_t k, int64_t ldx, void* y,
+                                  tp_dtype y_dtype, int64_t ldy, hipStream_t stream) {
+  if (!dtype_ok(x_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "x_dtype %d is not TP_F32 or TP_BF16", (int)x_dtype);
+  if (!dtype_ok(y_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "y_dtype %d is not TP_F32 or TP_BF16", (int)y_dtype);
+  TP_TRY(check_sizes(m, 0, k));
+  Extent ex, ey;
+  TP_TRY(check_matrix("x", x, m, k * dtype_size(x_dtype), ldx, dtype_size(x_dtype), &ex));
+  TP_TRY(check_matrix("y", y, m, k * dtype_size(y_dtype), ldy, dtype_size(y_dtype), &ey));
+  const bool in_place = (x == y && x_dtype == y_dtype && ldx == ldy);
+  if (!in_place && overlaps(ex, ey))
+    return fail(TP_ERR_BAD_ALIASING, "x and y overlap without being the same buffer, dtype and ld");
+  if (m == 0) return ok();
+  return hip_status(tp::launch_rotate_rows(x, x_dtype == TP_BF16, ldx, y, y_dtype == TP_BF16, ldy, m, k, stream),
+                    "rotate launch");
+}
+
+tp_status tp_quantize_rows_int8(const void* x, tp_dtype x_dtype, int64_t m, int64_t k, int64_t ldx, int a_flags,
+                                int8_t* qa, int64_t ldqa, float* sa, hipStream_t stream) {
+  if (!dtype_ok(x_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "x_dtype %d is not TP_F32 or TP_BF16", (int)x_dtype);
+  if (a_flags != TP_A_ROTATE && a_flags != TP_A_PREROTATED) return fail(TP_ERR_BAD_FLAGS, "a_flags=%d", a_flags);
+  TP_TRY(check_sizes(m, 0, k));
+  Extent ex, eq, es;
+  TP_TRY(check_matrix("x", x, m, k * dtype_size(x_dtype), ldx, dtype_size(x_dtype), &ex));
+  TP_TRY(check_matrix("qa", qa, m, k, ldqa, 1, &eq));
+  TP_TRY(check_vector("sa", sa, m, &es));
+  if (overlaps(ex, eq) || overlaps(ex, es) || overlaps(eq, es))
+    return fail(TP_ERR_BAD_ALIASING, "x, qa and sa must not overlap");
+  if (m == 0) return ok();
+  return hip_status(tp::launch_rotq_rows(x, x_dtype == TP_BF16, ldx, m, k, a_flags == TP_A_ROTATE, 8, qa, ldqa, sa,
+                                         stream),
+                    "activation quantize launch");
+}
+
+namespace {
+
+// Shared by the two weight-only products.
+tp_status weight_only(int kind, const void* a, tp_dtype a_dtype, int64_t lda, int a_flags, const void* q,
+                      int64_t ldq, const float* w_scales, int64_t m, int64_t n, int64_t k, void* c, tp_dtype c_dtype,
+                      int64_t ldc, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const tp_op op = kind == tp::GEMM_W8 ? TP_OP_QGEMM_W8 : TP_OP_QGEMM_W4;
+  if (a_flags != TP_A_ROTATE && a_flags != TP_A_PREROTATED) return fail(TP_ERR_BAD_FLAGS, "a_flags=%d", a_flags);
+  if (!dtype_ok(a_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "a_dtype %d is not TP_F32 or TP_BF16", (int)a_dtype);
+  if (a_flags == TP_A_PREROTATED && a_dtype != TP_BF16)
+    return fail(TP_ERR_UNSUPPORTED_DTYPE, "a pre-rotated operand must be TP_BF16");
+  if (!dtype_ok(c_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "c_dtype %d is not TP_F32 or TP_BF16", (int)c_dtype);
+  TP_TRY(check_sizes(m, n, k));
+  Extent ea, eq, es, ec, ew;
+  TP_TRY(check_matrix("a", a, m, k * dtype_size(a_dtype), lda, dtype_size(a_dtype), &ea));
+  TP_TRY(check_matrix("q", q, n, kind == tp::GEMM_W8 ? k : k / 2, ldq, 1, &eq));
+  int64_t ns;
+  if (!mul_ok(n, kind == tp::GEMM_W8 ? 1 : k / 256, &ns)) return fail(TP_ERR_SIZE_OVERFLOW, "scale count overflows");
+  TP_TRY(check_vector("w_scales", w_scales, ns, &es));
+  TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec));
+  int64_t need;
+  if (!workspace_bytes_for(op, m, k, a_flags, &need)) return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
+  if (need > 0) {
+    if (!ws || (int64_t)ws_bytes < need)
+      return fail(TP_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes given, %lld needed", ws_bytes, (long long)need);
+    if (((uintptr_t)ws & 15u) != 0) return fail(TP_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    ew.lo = (uintptr_t)ws;
+    ew.hi = ew.lo + (uintptr_t)need;
+  }
+  if (overlaps(ec, ea) || overlaps(ec, eq) || overlaps(ec, es) || overlaps(ec, ew) || overlaps(ew, ea) ||
+      overlaps(ew, eq) || overlaps(ew, es))
+    return fail(TP_ERR_BAD_ALIASING, "c and the workspace must not overlap any other operand");
+  if (m == 0 || n == 0) return ok();
+
+  const void* a_rot = a;
+  int64_t lda_rot = lda;
+  if (a_flags == TP_A_ROTATE) {
+    TP_TRY(hip_status(tp::launch_rotate_rows(a, a_dtype == TP_BF16, lda, ws, true, k, m, k, stream), "rotate launch"));
+    a_rot = ws;
+    lda_rot = k;
+  }
+  tp::GemmArgs g{};
+  g.kind = kind;
+  g.a = a_rot;
+  g.lda = lda_rot;
+  g.b = q;
+  g.ldb = ldq;
+  g.w_scales = w_scales;
+  g.a_scales = nullptr;
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  g.c = c;
+  g.c_bf16 = c_dtype == TP_BF16;
+  g.ldc = ldc;
+  g.acc_out = nullptr;
+  g.ld_acc = 0;
+  return hip_status(tp::launch_qgemm(g, stream), "product launch");
+}
+
+}  // namespace
+
+tp_status tp_qgemm_w8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags, const int8_t* q, int64_t ldq,
+                      const float* w_scales, int64_t m, int64_t n, int64_t k, void* c, tp_dtype c_dtype, int64_t ldc,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return weight_only(tp::GEMM_W8, a, a_dtype, lda, a_flags, q, ldq, w_scales, m, n, k, c, c_dtype, ldc, workspace,
+                     workspace_bytes, stream);
+}
+
+tp_status tp_qgemm_w4(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags, const uint8_t* q, int64_t ldq,
+                      const float* w_scales, int64_t m, int64_t n, int64_t k, void* c, tp_dtype c_dtype, int64_t ldc,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return weight_only(tp::GEMM_W4, a, a_dtype, lda, a_flags, q, ldq, w_scales, m, n, k, c, c_dtype, ldc, workspace,
+                     workspace_bytes, stream);
+}
+
+tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags, const int8_t* q, int64_t ldq,
+                        const float* w_scales, int64_t m, int64_t n, int64_t k, void* c, tp_dtype c_dtype,
+                        int64_t ldc, int8_t* qa_out, float* sa_out, int32_t* acc_out, int64_t ld_acc,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (a_flags != TP_A_ROTATE && a_flags != TP_A_PREROTATED) return fail(TP_ERR_BAD_FLAGS, "a_flags=%d", a_flags);
+  if (!dtype_ok(a_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "a_dtype %d is not TP_F32 or TP_BF16", (int)a_dtype);
+  if (!dtype_ok(c_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "c_dtype %d is not TP_F32 or TP_BF16", (int)c_dtype);
+  TP_TRY(check_sizes(m, n, k));
+  if (k > INT32_MAX / (127 * 127))
+    return fail(TP_ERR_BAD_SHAPE, "k=%lld: the int32 accumulator could overflow (k <= %d)", (long long)k,
+                INT32_MAX / (127 * 127));
+  Extent ea, eq, es, ec, eqa, esa, eacc, ew;
+  TP_TRY(check_matrix("a", a, m, k * dtype_size(a_dtype), lda, dtype_size(a_dtype), &ea));
+  TP_TRY(check_matrix("q", q, n, k, ldq, 1, &eq));
+  TP_TRY(check_vector("w_scales", w_scales, n, &es));
+  TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec));
+  const bool own_codes = qa_out && sa_out;
+  if (qa_out) TP_TRY(check_matrix("qa_out", qa_out, m, k, k, 1, &eqa));
+  if (sa_out) TP_TRY(check_vector("sa_out", sa_out, m, &esa));
+  if (acc_out) TP_TRY(check_matrix("acc_out", acc_out, m, n * 4, ld_acc, 4, &eacc));
+  int64_t need = 0;
+  if (!own_codes) {
+    if (!workspace_bytes_for(TP_OP_QGEMM_W8A8, m, k, a_flags, &need))
+      return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
+    if (!workspace || (int64_t)workspace_bytes < need)
+      return fail(TP_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes given, %lld needed", workspace_bytes,
+                  (long long)need);
+    if (((uintptr_t)workspace & 15u) != 0) return fail(TP_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    ew.lo = (uintptr_t)workspace;
+    ew.hi = ew.lo + (uintptr_t)need;
+  }
+  const Extent* outs[] = {&ec, &eqa, &esa, &eacc, &ew};
+  const Extent* ins[] = {&ea, &eq, &es};
+  for (const Extent* o : outs) {
+    for (const Extent* i : ins)
+      if (overlaps(*o, *i)) return fail(TP_ERR_BAD_ALIASING, "an output or the workspace overlaps an input");
+    for (const Extent* o2 : outs)
+      if (o2 != o && overlaps(*o, *o2)) return fail(TP_ERR_BAD_ALIASING, "two outputs overlap");
+  }
+  if (m == 0 || n == 0) return ok();
+
+  int8_t* qa = qa_out ? qa_out : (int8_t*)workspace;
+  float* sa = sa_out ? sa_out : (float*)((uint8_t*)workspace + round_up(m * k, 256));
+  TP_TRY(hip_status(tp::launch_rotq_rows(a, a_dtype == TP_BF16, lda, m, k, a_flags == TP_A_ROTATE, 8, qa, k, sa,
+                                         stream),
+                    "activation quantize launch"));
+  tp::GemmArgs g{};
+  g.kind = tp::GEMM_W8A8;
+  g.a = qa;
+  g.lda = k;
+  g.b = q;
+  g.ldb = ldq;
+  g.w_scales = w_scales;
+  g.a_scales = sa;
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  g.c = c;
+  g.c_bf16 = c_dtype == TP_BF16;
+  g.ldc = ldc;
+  g.acc_out = acc_out;
+  g.ld_acc = ld_acc;
+  return hip_status(tp::launch_qgemm(g, stream), "product launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal launchers of the gfx950 kernels. Callers (api.cpp) validate every
+// argument first; the launchers assume valid shapes, k % 256 == 0 and the
+// alignment rules of include/tp.h, and return the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+hipError_t launch_rotate_rows(const void* x, bool x_bf16, int64_t ldx, void* y, bool y_bf16, int64_t ldy,
+                              int64_t m, int64_t k, hipStream_t stream);
+
+// bits 8: int8 codes with one scale per row; bits 4: packed int4 codes with one
+// scale per (row, 256-group). rotate == false quantizes the rows as given.
+hipError_t launch_rotq_rows(const void* x, bool x_bf16, int64_t ldx, int64_t rows, int64_t k, bool rotate,
+                            int bits, void* q, int64_t ldq, float* scales, hipStream_t stream);
+
+enum GemmKind { GEMM_W8 = 0, GEMM_W4 = 1, GEMM_W8A8 = 2 };
+
+struct GemmArgs {
+  int kind;                 // GemmKind
+  const void* a;            // bf16 [m, k] (W8, W4) or int8 [m, k] (W8A8)
+  int64_t lda;              // elements
+  const void* b;            // int8 [n, k] or packed int4 [n, k/2]
+  int64_t ldb;              // bytes
+  const float* w_scales;    // [n] or [n, k/256]
+  const float* a_scales;    // [m] (W8A8) or nullptr
+  int64_t m, n, k;
+  void* c;                  // [m, n]
+  bool c_bf16;
+  int64_t ldc;              // elements
+  int32_t* acc_out;         // optional int32 [m, n] (W8A8)
+  int64_t ld_acc;
+};
+
+hipError_t launch_qgemm(const GemmArgs& args, hipStream_t stream);
+
+// Tile configuration chosen for a shape (exposed for the benchmark's reports).
+void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn);
+
+}  // namespace tp

@@ -1,0 +1,199 @@
+"""The C ABI without a GPU: libtp.so loads, exports every entry point that
+include/tp.h declares, and refuses every invalid call by name before any HIP
+call (so these run on a CPU-only host with made-up device addresses: nothing is
+dereferenced or launched)."""
+
+import os
+import re
+
+import pytest
+
+from int4_quantized_gemm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A, B, C, D, E = 0x10000, 0x4000000, 0x8000000, 0xC000000, 0x10000000  # disjoint fake addresses
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _lib.load()
+
+
+def _declared():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", f)).read()
+            names |= set(re.findall(r"^[a-z_ *]+?\b(tp_[a-z0-9_]+)\s*\(", text, flags=re.M))
+    return names
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"tp_rotate_quantize_weights", "tp_hadamard_rotate_rows", "tp_qgemm_w8", "tp_qgemm_w4",
+            "tp_qgemm_w8a8"} <= names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes declaration"
+
+
+def test_version_and_strings(lib):
+    assert lib.tp_abi_version() == 1
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.tp_status_string(code).decode() == name
+
+
+def _err(lib):
+    return lib.tp_last_error_message().decode()
+
+
+# --------------------------------------------------- rotate-quantize weights
+def rq(lib, w=A, dt=0, n=64, k=512, ldw=512, bits=8, q=B, ldq=512, s=C):
+    return lib.tp_rotate_quantize_weights(w, dt, n, k, ldw, bits, q, ldq, s, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=300, ldw=304, ldq=304), 3),
+    (dict(k=0), 2),
+    (dict(n=-1), 2),
+    (dict(w=0), 1),
+    (dict(q=0), 1),
+    (dict(s=0), 1),
+    (dict(w=A + 8), 5),
+    (dict(ldw=500), 4),
+    (dict(ldw=513), 5),
+    (dict(bits=5), 7),
+    (dict(bits=4, ldq=200), 4),
+    (dict(dt=7), 6),
+    (dict(s=C + 2), 5),
+    (dict(q=A + 1024), 10),
+    (dict(ldw=2 ** 62), 8),
+])
+def test_rotate_quantize_refusals(lib, kw, status):
+    assert rq(lib, **kw) == status, _err(lib)
+    assert _err(lib)
+
+
+def test_rotate_quantize_empty_is_noop(lib):
+    assert rq(lib, n=0) == 0
+
+
+# ------------------------------------------------------------- rotate rows
+def rr(lib, x=A, xd=1, m=8, k=512, ldx=512, y=B, yd=1, ldy=512):
+    return lib.tp_hadamard_rotate_rows(x, xd, m, k, ldx, y, yd, ldy, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=384, ldx=384, ldy=384), 3),
+    (dict(x=0), 1),
+    (dict(y=0), 1),
+    (dict(yd=3), 6),
+    (dict(ldy=256), 4),
+    (dict(y=A + 512), 10),              # partial overlap
+    (dict(y=A, yd=0, ldy=512), 10),     # same base, other dtype: not in place
+    (dict(y=A, ldy=1024), 10),          # same base, other pitch
+    (dict(x=A + 4), 5),
+])
+def test_rotate_rows_refusals(lib, kw, status):
+    assert rr(lib, **kw) == status, _err(lib)
+
+
+def test_rotate_rows_empty_and_inplace_validate(lib):
+    assert rr(lib, m=0) == 0
+    assert rr(lib, m=0, y=A, ldy=512) == 0
+
+
+# -------------------------------------------------------- quantize rows int8
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=2), 11),
+    (dict(k=100, ldx=128, ldqa=128), 3),
+    (dict(qa=0), 1),
+    (dict(sa=0), 1),
+    (dict(ldqa=500), 4),
+    (dict(qa=A), 10),
+])
+def test_quantize_rows_refusals(lib, kw, status):
+    a = dict(x=A, xd=1, m=8, k=512, ldx=512, flags=1, qa=B, ldqa=512, sa=C)
+    a.update(kw)
+    got = lib.tp_quantize_rows_int8(a["x"], a["xd"], a["m"], a["k"], a["ldx"], a["flags"], a["qa"], a["ldqa"],
+                                    a["sa"], None)
+    assert got == status, _err(lib)
+
+
+# ------------------------------------------------------------ products
+def w8(lib, fn="tp_qgemm_w8", a=A, ad=1, lda=512, flags=1, q=B, ldq=512, s=C, m=64, n=256, k=512, c=D, cd=1,
+       ldc=256, ws=E, wsb=64 * 512 * 2):
+    return getattr(lib, fn)(a, ad, lda, flags, q, ldq, s, m, n, k, c, cd, ldc, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=768 + 1, lda=1024, ldq=1024), 3),
+    (dict(flags=5), 11),
+    (dict(flags=0, ad=0), 6),            # pre-rotated operand must be bf16
+    (dict(cd=9), 6),
+    (dict(ws=0), 9),
+    (dict(wsb=100), 9),
+    (dict(ws=E + 8), 5),
+    (dict(c=A + 256), 10),
+    (dict(ws=B), 10),
+    (dict(ldc=100), 4),
+    (dict(ldq=256), 4),
+    (dict(m=-3), 2),
+    (dict(m=2 ** 40), 2),
+])
+def test_w8_refusals(lib, kw, status):
+    assert w8(lib, **kw) == status, _err(lib)
+
+
+def test_w4_checks_packed_rows(lib):
+    assert w8(lib, fn="tp_qgemm_w4", ldq=128, m=0) == 4
+    assert w8(lib, fn="tp_qgemm_w4", ldq=256, m=0) == 0
+
+
+def test_products_empty_are_noops(lib):
+    assert w8(lib, m=0) == 0
+    assert w8(lib, n=0) == 0
+    assert w8(lib, fn="tp_qgemm_w4", ldq=256, n=0) == 0
+
+
+def w8a8(lib, a=A, ad=1, lda=512, flags=1, q=B, ldq=512, s=C, m=64, n=256, k=512, c=D, cd=0, ldc=256, qa=0, sa=0,
+         acc=0, ld_acc=0, ws=E, wsb=1 << 20):
+    return lib.tp_qgemm_w8a8(a, ad, lda, flags, q, ldq, s, m, n, k, c, cd, ldc, qa or None, sa or None, acc or None,
+                             ld_acc, ws or None, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=133376, lda=133376, ldq=133376), 2),     # int32 accumulator could overflow
+    (dict(ws=0), 9),
+    (dict(wsb=1000), 9),
+    (dict(acc=0x20000000, ld_acc=100), 4),
+    (dict(acc=D, ld_acc=256), 10),                   # acc_out overlaps c
+    (dict(c=B), 10),                                 # c overlaps q
+    (dict(flags=-1), 11),
+    (dict(qa=0x30000000, sa=0x30000000 + 64 * 512 - 4, ws=0, wsb=0), 10),
+])
+def test_w8a8_refusals(lib, kw, status):
+    assert w8a8(lib, **kw) == status, _err(lib)
+
+
+def test_w8a8_own_codes_need_no_workspace(lib):
+    assert w8a8(lib, m=0, qa=0x30000000, sa=0x38000000, ws=0, wsb=0) == 0
+
+
+def test_workspace_sizes(lib):
+    assert lib.tp_workspace_size(1, 4096, 12288, 3072, 1) == 4096 * 3072 * 2
+    assert lib.tp_workspace_size(2, 4032, 3072, 12288, 1) == 4032 * 12288 * 2
+    assert lib.tp_workspace_size(1, 4096, 12288, 3072, 0) == 0
+    assert lib.tp_workspace_size(3, 4096, 9216, 3072, 1) == 4096 * 3072 + 4096 * 4
+    assert lib.tp_workspace_size(3, 3, 9216, 256, 1) == 768 + 12
+    assert lib.tp_workspace_size(3, -1, 9, 256, 1) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import int4_quantized_gemm_amd as tp
+    with pytest.raises(ValueError):
+        tp.tp_hadamard_rotate_rows(torch.zeros(4, 256))

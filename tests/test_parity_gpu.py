@@ -1,0 +1,378 @@
+"""HIP path vs the CPU oracle, element by element, on the same seeded inputs.
+
+* weight rotate-and-quantize: codes (int8, packed int4) and fp32 scales
+  bit-exact, at full size for every workload's weight;
+* activation rotation: within the fp32 transform's error bound (fp32 out), or
+  equal to a correct bf16 rounding of a value within that bound (bf16 out);
+* per-token activation quantization: codes and scales bit-exact;
+* W8 / W4 products: relative Frobenius error <= 2e-3 against the oracle that
+  models the bf16 activation operand;
+* W8A8: int32 accumulators, codes and scales bit-exact; output within 1e-5.
+
+Small workloads are compared in full; full-size workloads run in the launch
+configuration the benchmark times and are compared on sampled rows (whole
+output rows, every column, including tile tails).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import int4_quantized_gemm_amd as tp
+import oracle
+import workloads as W
+from tests.gpu_util import (announce, assert_bf16_path, assert_w8a8_out, dev, f64, host,
+                            rotation_error_bound, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ helpers
+def _weights_i8(w_cpu, d):
+    q, s = tp.tp_rotate_quantize_weights(w_cpu.to(d), bits=8)
+    return q, s
+
+
+def _check_weights(w_cpu, bits, d):
+    q, s = tp.tp_rotate_quantize_weights(w_cpu.to(d), bits=bits)
+    torch.cuda.synchronize()
+    if bits == 8:
+        rq, rs = oracle.quantize_weights_int8(w_cpu.float().numpy())
+        assert np.array_equal(host(q), rq), "int8 codes differ"
+    else:
+        rq, rs = oracle.quantize_weights_int4(w_cpu.float().numpy())
+        assert np.array_equal(host(q), rq), "packed int4 codes differ"
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32)), "scales differ"
+    return q, s
+
+
+# ------------------------------------------------- weight rotate + quantize
+@pytest.mark.parametrize("name", ["tiny", "proj256", "ffn_up", "dit_qkv", "dit_out", "dit_gateup", "dit_down"])
+def test_rotate_quantize_int8_full(name):
+    d = dev()
+    wl = W.BY_NAME[name]
+    announce("tp_rotate_quantize_weights bits=8", name, wl.n, wl.k, "seed", wl.seed)
+    _, w = W.generate(wl, rows=1)
+    _check_weights(w, 8, d)
+
+
+@pytest.mark.parametrize("name", ["tiny", "proj256", "ffn_down"])
+def test_rotate_quantize_int4_full(name):
+    d = dev()
+    wl = W.BY_NAME[name]
+    announce("tp_rotate_quantize_weights bits=4", name, wl.n, wl.k, "seed", wl.seed)
+    _, w = W.generate(wl, rows=1)
+    _check_weights(w, 4, d)
+
+
+def test_rotate_quantize_edge_rows():
+    d = dev()
+    announce("tp_rotate_quantize_weights edge rows")
+    w = W.random_rows((7, 768), seed=5, scale=0.02)
+    w[2] = 0.0                      # zero row -> scale 0, codes 0
+    w[3, 256:512] = 0.0             # zero group (int4)
+    w[4, 10] = 1e3                  # one huge outlier
+    w[5] = torch.arange(768, dtype=torch.float32) - 384.0   # dyadic values: exact rotation
+    for bits in (8, 4):
+        _check_weights(w, bits, d)
+    # bf16 source weights
+    wb = W.random_rows((5, 512), seed=6, dtype="bf16", scale=0.02)
+    for bits in (8, 4):
+        q, s = tp.tp_rotate_quantize_weights(wb.to(d), bits=bits)
+        if bits == 8:
+            rq, rs = oracle.quantize_weights_int8(wb.float().numpy())
+        else:
+            rq, rs = oracle.quantize_weights_int4(wb.float().numpy())
+        assert np.array_equal(host(q), rq) and np.array_equal(host(s), rs)
+
+
+def test_rotate_quantize_padded_subview():
+    d = dev()
+    announce("tp_rotate_quantize_weights padded sub-view")
+    big = W.random_rows((40, 1024 + 256), seed=7, scale=0.02).to(d)
+    w = big[3:35, 256:1280]        # storage offset, ld = 1280
+    qbuf = torch.zeros((32, 1024 + 64), dtype=torch.int8, device=d)
+    q = qbuf[:, :1024]             # ld = 1088 bytes
+    s = torch.empty(32, dtype=torch.float32, device=d)
+    tp.tp_rotate_quantize_weights(w, bits=8, q=q, scales=s)
+    rq, rs = oracle.quantize_weights_int8(w.float().cpu().numpy())
+    assert np.array_equal(host(q), rq) and np.array_equal(host(s), rs)
+    assert torch.all(qbuf[:, 1024:] == 0), "wrote past the row"
+
+
+# ------------------------------------------------------- activation rotation
+@pytest.mark.parametrize("xd,yd", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("m,k", [(64, 512), (37, 768), (1, 256), (288, 3072)])
+def test_rotate_rows(xd, yd, m, k):
+    d = dev()
+    announce("tp_hadamard_rotate_rows", xd, yd, m, k)
+    x = W.random_rows((m, k), seed=m + k, dtype=xd)
+    x[:, 3] *= 30.0
+    ydt = torch.float32 if yd == "f32" else torch.bfloat16
+    y = tp.tp_hadamard_rotate_rows(x.to(d), out_dtype=ydt)
+    x64 = f64(x)
+    exact = oracle.rotate_groups(x64)
+    bound = rotation_error_bound(x64)
+    got = f64(y)
+    if yd == "f32":
+        assert np.all(np.abs(got - exact) <= bound), "fp32 rotation outside its error bound"
+    else:
+        lo = oracle.bf16_round(exact - bound)
+        hi = oracle.bf16_round(exact + bound)
+        assert np.all((got == lo) | (got == hi)), "bf16 rotation is not a rounding of a value within the bound"
+        assert np.mean(got != oracle.bf16_round(exact)) < 1e-3
+
+
+def test_rotate_rows_in_place_and_subview():
+    d = dev()
+    announce("tp_hadamard_rotate_rows in place / sub-view")
+    base = W.random_rows((50, 1024 + 512), seed=9, dtype="bf16").to(d)
+    ref_in = base.clone()
+    view = base[5:45, 256:1280]
+    tp.tp_hadamard_rotate_rows(view, out=view)          # in place on a padded view
+    exact = oracle.rotate_groups(f64(ref_in[5:45, 256:1280]))
+    bound = rotation_error_bound(f64(ref_in[5:45, 256:1280]))
+    got = f64(view)
+    lo, hi = oracle.bf16_round(exact - bound), oracle.bf16_round(exact + bound)
+    assert np.all((got == lo) | (got == hi))
+    # untouched outside the view
+    assert torch.equal(base[:5], ref_in[:5]) and torch.equal(base[45:], ref_in[45:])
+    assert torch.equal(base[:, :256], ref_in[:, :256]) and torch.equal(base[:, 1280:], ref_in[:, 1280:])
+
+
+def test_rotate_rows_inverse():
+    """Rotating twice gives back the input (Q Q = I) up to fp32 rounding."""
+    d = dev()
+    announce("tp_hadamard_rotate_rows twice")
+    x = W.random_rows((33, 1536), seed=10).to(d)
+    y = tp.tp_hadamard_rotate_rows(tp.tp_hadamard_rotate_rows(x))
+    assert torch.allclose(y, x, rtol=0, atol=1e-5)
+
+
+# ------------------------------------------- per-token activation quantization
+@pytest.mark.parametrize("name,rows", [("tiny", None), ("dit_qkv", None), ("dit_down", 512), ("proj256", None)])
+@pytest.mark.parametrize("rotate", [True, False])
+def test_quantize_rows_int8(name, rows, rotate):
+    d = dev()
+    wl = W.BY_NAME[name]
+    announce("tp_quantize_rows_int8", name, rows, "rotate", rotate)
+    x = W.generate_activations(wl, rows=rows)
+    qa, sa = tp.tp_quantize_rows_int8(x.to(d), rotate=rotate)
+    rqa, rsa = oracle.quantize_activations_int8(f64(x), rotate=rotate)
+    assert np.array_equal(host(sa).view(np.uint32), rsa.view(np.uint32)), "scales differ"
+    assert np.array_equal(host(qa), rqa), f"{int(np.sum(host(qa) != rqa))} codes differ"
+
+
+def test_quantize_rows_zero_and_tiny_rows():
+    d = dev()
+    announce("tp_quantize_rows_int8 zero rows")
+    x = W.random_rows((6, 512), seed=11)
+    x[1] = 0.0
+    x[2] = 1e-30
+    x[3, 7] = -5.0
+    qa, sa = tp.tp_quantize_rows_int8(x.to(d))
+    rqa, rsa = oracle.quantize_activations_int8(f64(x))
+    assert np.array_equal(host(sa), rsa) and np.array_equal(host(qa), rqa)
+    assert host(sa)[1] == 0 and np.all(host(qa)[1] == 0)
+
+
+# ------------------------------------------------------------- W8 / W4 products
+def _w8_case(wl, rows=None, row_sel=None, out_dtype=None):
+    d = dev()
+    x, w = W.generate(wl)
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    odt = out_dtype or (torch.float32 if wl.out_dtype == "f32" else torch.bfloat16)
+    y = tp.tp_qgemm_w8(x.to(d), q, s, rotate=True, out_dtype=odt)
+    sel = row_sel if row_sel is not None else np.arange(wl.m)
+    ref = oracle.qgemm_w8(f64(x)[sel], host(q), host(s))
+    return f64(y)[sel], ref
+
+
+def _w4_case(wl, row_sel=None, out_dtype=None):
+    d = dev()
+    x, w = W.generate(wl)
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=4)
+    odt = out_dtype or (torch.float32 if wl.out_dtype == "f32" else torch.bfloat16)
+    y = tp.tp_qgemm_w4(x.to(d), q, s, rotate=True, out_dtype=odt)
+    sel = row_sel if row_sel is not None else np.arange(wl.m)
+    ref = oracle.qgemm_w4(f64(x)[sel], host(q), host(s))
+    return f64(y)[sel], ref
+
+
+def test_w8_tiny_full():
+    announce("tp_qgemm_w8 tiny 64x512x256 fp32 out")
+    got, ref = _w8_case(W.TINY)
+    err = assert_bf16_path(got, ref, "w8 tiny")
+    assert err < 1e-4, "fp32 output: only A-operand rounding flips and fp32 sums remain"
+
+
+def test_w8_proj256_full():
+    announce("tp_qgemm_w8 proj256 288x3072x3072 bf16 out")
+    got, ref = _w8_case(W.PROJ256)
+    assert_bf16_path(got, ref, "w8 proj256")
+
+
+def test_w8_ffn_up_sampled():
+    wl = W.FFN_UP
+    announce("tp_qgemm_w8 ffn_up 4096x3072x12288 (sampled rows)")
+    got, ref = _w8_case(wl, row_sel=sample_rows(wl.m, 48, seed=1))
+    assert_bf16_path(got, ref, "w8 ffn_up")
+
+
+def test_w4_tiny_full():
+    announce("tp_qgemm_w4 tiny 64x512x256 fp32 out")
+    got, ref = _w4_case(W.TINY.with_(path="w4"))
+    err = assert_bf16_path(got, ref, "w4 tiny")
+    assert err < 1e-4
+
+
+def test_w4_ffn_down_sampled():
+    wl = W.FFN_DOWN
+    announce("tp_qgemm_w4 ffn_down 4032x12288x3072 (sampled rows)")
+    got, ref = _w4_case(wl, row_sel=sample_rows(wl.m, 48, seed=2))
+    assert_bf16_path(got, ref, "w4 ffn_down")
+
+
+@pytest.mark.parametrize("kind", ["w8", "w4"])
+@pytest.mark.parametrize("m,n,k", [(1, 256, 256), (100, 200, 768), (129, 385, 512), (300, 130, 1280)])
+def test_weight_only_ragged(kind, m, n, k):
+    d = dev()
+    announce("tp_qgemm", kind, "ragged", m, n, k)
+    wl = W.TINY.with_(m=m, n=n, k=k, seed=m * 7 + n, act_outliers=2, w_outliers=2)
+    x, w = W.generate(wl)
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8 if kind == "w8" else 4)
+    fn = tp.tp_qgemm_w8 if kind == "w8" else tp.tp_qgemm_w4
+    y = fn(x.to(d), q, s, rotate=True, out_dtype=torch.float32)
+    ref = (oracle.qgemm_w8 if kind == "w8" else oracle.qgemm_w4)(f64(x), host(q), host(s))
+    err = assert_bf16_path(f64(y), ref, f"{kind} ragged")
+    assert err < 1e-4
+
+
+def test_w8_prerotated_padded_views():
+    d = dev()
+    announce("tp_qgemm_w8 pre-rotated bf16 A, padded A and C views")
+    wl = W.TINY.with_(m=96, n=320, k=1024, seed=12)
+    x, w = W.generate(wl)
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    xr = tp.tp_hadamard_rotate_rows(x.to(d), out_dtype=torch.bfloat16)
+    abuf = torch.zeros((100, 1024 + 256), dtype=torch.bfloat16, device=d)
+    abuf[2:98, 128:1152] = xr
+    cbuf = torch.full((100, 320 + 64), 7.0, dtype=torch.float32, device=d)
+    out = cbuf[3:99, 32:352]
+    tp.tp_qgemm_w8(abuf[2:98, 128:1152], q, s, rotate=False, out=out)
+    ref = oracle.qgemm_w8(f64(xr), host(q), host(s), rotate=False)
+    assert_bf16_path(f64(out), ref, "w8 prerotated view")
+    assert torch.all(cbuf[:3] == 7.0) and torch.all(cbuf[99:] == 7.0)
+    assert torch.all(cbuf[:, :32] == 7.0) and torch.all(cbuf[:, 352:] == 7.0)
+
+
+# ------------------------------------------------------------------ W8A8
+def _w8a8_case(wl, row_sel=None):
+    d = dev()
+    x, w = W.generate(wl)
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    y, qa, sa, acc = tp.tp_qgemm_w8a8(x.to(d), q, s, rotate=True, want_codes=True, want_acc=True)
+    sel = row_sel if row_sel is not None else np.arange(wl.m)
+    ry, racc, rqa, rsa = oracle.qgemm_w8a8(f64(x)[sel], host(q), host(s))
+    assert np.array_equal(host(sa)[sel], rsa), "activation scales differ"
+    assert np.array_equal(host(qa)[sel], rqa), "activation codes differ"
+    gacc = host(acc)[sel].astype(np.int64)
+    assert np.array_equal(gacc, racc), f"{int(np.sum(gacc != racc))} int32 accumulators differ"
+    assert_w8a8_out(f64(y)[sel], ry, f"w8a8 {wl.name}")
+    # the caller-visible output without the intermediates is the same bytes
+    y2 = tp.tp_qgemm_w8a8(x.to(d), q, s, rotate=True)
+    assert torch.equal(y, y2)
+
+
+def test_w8a8_tiny_full():
+    announce("tp_qgemm_w8a8 tiny 64x512x256")
+    _w8a8_case(W.TINY.with_(path="w8a8"))
+
+
+@pytest.mark.parametrize("name", ["dit_qkv", "dit_out", "dit_gateup", "dit_down"])
+def test_w8a8_dit_block_sampled(name):
+    wl = W.BY_NAME[name]
+    announce("tp_qgemm_w8a8", name, wl.m, wl.k, wl.n, "(sampled rows)")
+    _w8a8_case(wl, row_sel=sample_rows(wl.m, 40, seed=wl.seed))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 256, 256), (100, 200, 768), (129, 385, 512), (257, 131, 1024)])
+def test_w8a8_ragged(m, n, k):
+    announce("tp_qgemm_w8a8 ragged", m, n, k)
+    _w8a8_case(W.TINY.with_(m=m, n=n, k=k, seed=m + 3 * n, act_outliers=2, w_outliers=2, path="w8a8"))
+
+
+def test_w8a8_planted_integers():
+    """X = X'.Q and W = W'.Q with integer X', W' whose row maxima are 127:
+    the device must return qa = X', sa = 1, acc = X' W'^T, y = acc."""
+    d = dev()
+    announce("tp_qgemm_w8a8 planted integers")
+    rng = np.random.default_rng(30)
+    m, n, k = 40, 72, 512
+    xv = rng.integers(-127, 128, size=(m, k))
+    wv = rng.integers(-127, 128, size=(n, k))
+    xv[:, 5] = 127
+    wv[:, 9] = -127
+    H = oracle.hadamard_matrix(256) / 16.0
+    rot = lambda a: np.concatenate([a[:, g * 256:(g + 1) * 256] @ H for g in range(k // 256)], axis=1)
+    x = torch.from_numpy(rot(xv.astype(np.float64)).astype(np.float32))
+    w = torch.from_numpy(rot(wv.astype(np.float64)).astype(np.float32))
+    assert np.array_equal(oracle.rotate_groups(x.numpy()), xv)  # the planted inputs are exact in fp32
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    assert np.array_equal(host(q), wv) and np.all(host(s) == 1.0)
+    y, qa, sa, acc = tp.tp_qgemm_w8a8(x.to(d), q, s, want_codes=True, want_acc=True)
+    ref = xv @ wv.T
+    assert np.array_equal(host(qa), xv) and np.all(host(sa) == 1.0)
+    assert np.array_equal(host(acc), ref)
+    assert np.array_equal(f64(y), ref.astype(np.float64))
+
+
+def test_w8a8_max_codes_at_large_k():
+    """All codes +-127 at K = 12288: acc = +-127^2 K, inside int32."""
+    d = dev()
+    announce("tp_qgemm_w8a8 extreme codes K=12288")
+    m, n, k = 32, 48, 12288
+    ones = torch.ones((m, k), dtype=torch.float32)
+    ones[1::2] *= -1
+    # rotated operand equal to the all-ones rows: pass it pre-rotated
+    q = torch.full((n, k), 127, dtype=torch.int8, device=d)
+    s = torch.ones(n, dtype=torch.float32, device=d)
+    y, qa, sa, acc = tp.tp_qgemm_w8a8(ones.to(d), q, s, rotate=False, want_codes=True, want_acc=True)
+    expect = np.where(np.arange(m)[:, None] % 2 == 0, 1, -1) * 127 * 127 * k * np.ones((1, n), dtype=np.int64)
+    assert np.array_equal(host(acc).astype(np.int64), expect)
+
+
+def test_determinism():
+    d = dev()
+    announce("determinism: repeated calls give identical bytes")
+    wl = W.PROJ256
+    x, w = W.generate(wl)
+    xd = x.to(d)
+    q8, s8 = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    q4, s4 = tp.tp_rotate_quantize_weights(w.to(d), bits=4)
+    outs = []
+    for _ in range(2):
+        outs.append((tp.tp_qgemm_w8(xd, q8, s8), tp.tp_qgemm_w4(xd, q4, s4), tp.tp_qgemm_w8a8(xd, q8, s8),
+                     tp.tp_hadamard_rotate_rows(xd)))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_empty_inputs_are_noops():
+    d = dev()
+    announce("empty m / n")
+    x = torch.empty((0, 512), dtype=torch.bfloat16, device=d)
+    q = torch.zeros((16, 512), dtype=torch.int8, device=d)
+    s = torch.ones(16, dtype=torch.float32, device=d)
+    assert tp.tp_qgemm_w8(x, q, s).shape == (0, 16)
+    assert tp.tp_qgemm_w8a8(x, q, s).shape == (0, 16)
+    assert tp.tp_hadamard_rotate_rows(x).shape == (0, 512)
+
+
+def test_refusal_reaches_python():
+    d = dev()
+    announce("refusal surfaces as TPError")
+    x = torch.zeros((4, 300), dtype=torch.bfloat16, device=d)
+    with pytest.raises(tp.TPError) as e:
+        tp.tp_hadamard_rotate_rows(x)
+    assert e.value.status_name == "TP_ERR_K_NOT_MULTIPLE_OF_256"
