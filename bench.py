@@ -1,0 +1,275 @@
+"""Throughput of the rotated, quantized projections on one MI355X.
+
+One step = one pass of the whole per-step hot path over the projections of one
+diffusion-transformer block at 1024x1024 (M = 4096 latent rows):
+
+  W8A8  qkv 3072->9216, out 3072->3072, gate+up 3072->24576, down 12288->3072:
+        rotate + per-token int8 quantize (tp_quantize_rows_int8), then the i8
+        product with its fused scale epilogue (tp_qgemm_w8a8_prequantized);
+  W8    FFN up 3072->12288: rotate to bf16 (tp_hadamard_rotate_rows), then the
+        weight-only int8 product (tp_qgemm_w8);
+  W4    FFN down 12288->3072 at M = 4032: rotate, then the weight-only int4
+        product (tp_qgemm_w4).
+
+Weights are rotated and quantized once before timing (offline by definition);
+that step is timed separately and reported as weight_prep. All inputs are
+seeded synthetic tensors with the value distributions described in
+workloads/__init__.py (Gaussian activations with outlier channels, Gaussian
+weights with outlier input columns); no checkpoint or dataset is involved.
+
+Printed: one JSON line with the step throughput (TOPS over all products of the
+step), the dominant kernel's roofline fraction (HIP events around each launch
+inside the timed region), a per-launch breakdown and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TOPS_I8 = 5000.0       # MI355X dense int8 MFMA, TOP/s
+PEAK_TFLOPS_BF16 = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
+METRIC = "rotated int8/int4 QGEMM TOPS & % MFMA/HBM roofline at M=4096,K=3072 (1 GPU)"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=0,
+                   help="activation rows of the CPU oracle sample (0: all rows of every product)")
+    p.add_argument("--cpu-only", action="store_true", help="time only the CPU oracle sample (no GPU)")
+    return p.parse_args()
+
+
+def step_plan():
+    import workloads as W
+    return [("w8a8", W.DIT_QKV), ("w8a8", W.DIT_OUT), ("w8a8", W.DIT_GATEUP), ("w8a8", W.DIT_DOWN),
+            ("w8", W.FFN_UP), ("w4", W.FFN_DOWN)]
+
+
+def _src_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "rotate.hip", "device_common.hpp"):
+        with open(os.path.join(ROOT, "int4_quantized_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_for(kernel_key):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != _src_hash():
+        return None
+    v = rec.get("kernels", {}).get(kernel_key)
+    return None if v is None else v.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------- CPU baseline
+def cpu_baseline(rows):
+    """The oracle as it stands, on the first `rows` activation rows of every
+    product of the step (weights quantized by the oracle first, untimed)."""
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    total_ops = 0.0
+    total_s = 0.0
+    parts = []
+    for kind, wl in step_plan():
+        x, w = W.generate(wl, rows=rows or None)
+        x64 = x.double().numpy()
+        wn = w.numpy()
+        if kind == "w4":
+            q, s = oracle.quantize_weights_int4(wn)
+            fn = lambda: oracle.qgemm_w4(x64, q, s)
+        else:
+            q, s = oracle.quantize_weights_int8(wn)
+            fn = (lambda: oracle.qgemm_w8(x64, q, s)) if kind == "w8" else (lambda: oracle.qgemm_w8a8(x64, q, s))
+        del w, wn
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        dt = float(np.median(times))
+        ops = 2.0 * x.shape[0] * wl.n * wl.k
+        total_ops += ops
+        total_s += dt
+        parts.append(f"{wl.name}:{dt:.2f}s")
+    return {
+        "value": total_ops / total_s / 1e12,
+        "unit": "TOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{'first %d' % rows if rows else 'all'} activation rows of each of the 6 products of the step "
+                  f"(all N, all K), "
+                  f"fp64 numpy oracle incl. rotation, quantization, dequantization and product; median of 3 runs, "
+                  f"{total_s:.1f} s per pass ({', '.join(parts)})",
+    }
+
+
+# ------------------------------------------------------------------ GPU path
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.cpu_only:
+        print(json.dumps(cpu_baseline(args.cpu_rows)))
+        return
+
+    import torch
+    import int4_quantized_gemm_amd as tp
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+
+    # ---- inputs and offline weight preparation (untimed)
+    plan = []
+    prep_s = 0.0
+    prep_bytes = 0
+    for kind, wl in step_plan():
+        x, w = W.generate(wl)
+        xd = x.to(d)
+        wd = w.to(d)
+        del x, w
+        bits = 4 if kind == "w4" else 8
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        q, s = tp.tp_rotate_quantize_weights(wd, bits=bits)
+        torch.cuda.synchronize()
+        prep_s += time.perf_counter() - t0
+        prep_bytes += wd.numel() * 4
+        del wd
+        e = {"kind": kind, "wl": wl, "x": xd, "q": q, "s": s}
+        if kind == "w8a8":
+            e["qa"] = torch.empty((wl.m, wl.k), dtype=torch.int8, device=d)
+            e["sa"] = torch.empty((wl.m,), dtype=torch.float32, device=d)
+            e["out"] = torch.empty((wl.m, wl.n), dtype=torch.float32, device=d)
+        else:
+            e["xr"] = torch.empty((wl.m, wl.k), dtype=torch.bfloat16, device=d)
+            e["out"] = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=d)
+        plan.append(e)
+    ws = torch.empty((256,), dtype=torch.uint8, device=d)
+
+    # one launch list per step: (name, roofline kind, algorithmic units, callable)
+    launches = []
+    for e in plan:
+        wl = e["wl"]
+        if e["kind"] == "w8a8":
+            launches.append((f"rotate_quantize_i8[{wl.name}]", "hbm", wl.m * wl.k * (2 + 1) + wl.m * 4,
+                             lambda e=e: tp.tp_quantize_rows_int8(e["x"], qa=e["qa"], sa=e["sa"])))
+            launches.append((f"gemm_w8a8[{wl.name}]", "i8", 2.0 * wl.m * wl.n * wl.k,
+                             lambda e=e: tp.tp_qgemm_w8a8_prequantized(e["qa"], e["sa"], e["q"], e["s"],
+                                                                       out=e["out"])))
+        else:
+            launches.append((f"rotate_bf16[{wl.name}]", "hbm", wl.m * wl.k * (2 + 2),
+                             lambda e=e: tp.tp_hadamard_rotate_rows(e["x"], out=e["xr"])))
+            fn = tp.tp_qgemm_w8 if e["kind"] == "w8" else tp.tp_qgemm_w4
+            launches.append((f"gemm_{e['kind']}[{wl.name}]", "bf16", 2.0 * wl.m * wl.n * wl.k,
+                             lambda e=e, fn=fn: fn(e["xr"], e["q"], e["s"], rotate=False, out=e["out"],
+                                                   workspace=ws)))
+    step_ops = sum(u for _, k, u, _ in launches if k != "hbm")
+
+    def run_step(events=None):
+        for i, (_, _, _, fn) in enumerate(launches):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in launches]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_i in range(args.steps):
+        run_step(ev[s_i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = []
+    for i, (name, kind, units, _) in enumerate(launches):
+        ms = float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+        sec = ms * 1e-3
+        if kind == "hbm":
+            ach, peak, unit = units / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+        elif kind == "i8":
+            ach, peak, unit = units / sec / 1e12, PEAK_TOPS_I8, "TOP/s"
+        else:
+            ach, peak, unit = units / sec / 1e12, PEAK_TFLOPS_BF16, "TFLOP/s"
+        per.append({"launch": name, "us": round(ms * 1e3, 2), "achieved": round(ach, 1), "unit": unit,
+                    "peak": peak, "frac": round(ach / peak, 4), "bound": "hbm" if kind == "hbm" else "mfma",
+                    "units": units})
+    dom = max(per, key=lambda r: r["us"])
+    ms_per_step = wall / args.steps * 1e3
+    value = step_ops / (wall / args.steps) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+bf16",
+        "data": "synthetic (seeded Gaussian activations with outlier channels, Gaussian weights with outlier "
+                "input columns; no checkpoint)",
+        "config": {
+            "workload": "dit_block_1024: W8A8 qkv/out/gate+up/down (M=4096) + W8 FFN up (M=4096, K=3072, "
+                        "N=12288) + W4 FFN down (M=4032, K=12288, N=3072), activation rotation included",
+            "m": 4096,
+            "step_ops": step_ops,
+        },
+        "roofline": {
+            "kernel": dom["launch"],
+            "bound": dom["bound"],
+            "achieved": dom["achieved"],
+            "peak": dom["peak"],
+            "unit": dom["unit"],
+            "frac": dom["frac"],
+            "traffic": _traffic_for(dom["launch"]),
+        },
+        "breakdown": [{k: r[k] for k in ("launch", "us", "achieved", "unit", "frac")} for r in per],
+        "weight_prep": {"gbs_fp32_read": round(prep_bytes / prep_s / 1e9, 1), "seconds": round(prep_s, 4),
+                        "note": "tp_rotate_quantize_weights over every weight of the step, once, untimed in value"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

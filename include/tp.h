@@ -26,9 +26,11 @@
  * Pointers    All data pointers are DEVICE pointers owned by the caller. The
  *             library keeps no pointer after a call returns and allocates no
  *             memory: scratch comes from the caller's workspace, sized with
- *             tp_workspace_size(). Base pointers must be 16-byte aligned and
- *             every row pitch (ld * element size) a multiple of 16 bytes;
- *             scale arrays must be 4-byte aligned.
+ *             tp_workspace_size(). Base pointers of inputs, codes and the
+ *             workspace must be 16-byte aligned and their row pitch (ld *
+ *             element size) a multiple of 16 bytes; outputs C and acc_out
+ *             need only the alignment of their element type; scale arrays
+ *             must be 4-byte aligned. An operand with no elements may be NULL.
  * Streams     Work is enqueued on `stream` (NULL = the default stream) and runs
  *             asynchronously; no call synchronizes or copies to the host.
  *             Calls that overlap on different streams and share buffers race.
@@ -211,6 +213,25 @@ tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flag
                         int64_t n, int64_t k, void* c, tp_dtype c_dtype, int64_t ldc,
                         int8_t* qa_out, float* sa_out, int32_t* acc_out, int64_t ld_acc,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tp_qgemm_w8a8_prequantized -- the int8 x int8 product of tp_qgemm_w8a8 on
+ * activation codes the caller already holds (from tp_quantize_rows_int8 or an
+ * earlier tp_qgemm_w8a8 with qa_out / sa_out), so that one quantized
+ * activation can feed several weight matrices (tensai docs, "画像生成", section
+ * "GPU": the feed-forward's projections run as one batch on the device).
+ *
+ *   qa       int8 [m, k] codes, row pitch ldqa bytes; sa fp32 [m] scales.
+ *   q        int8 [n, k] weight codes, row pitch ldq; w_scales fp32 [n].
+ *   c        [m, n], TP_F32 or TP_BF16, row pitch ldc:
+ *            C[r, c] = (float(acc[r, c]) * sa[r]) * w_scales[c].
+ *   acc_out  optional int32 [m, n] raw accumulators, row pitch ld_acc.
+ *   No workspace. k <= 133144.
+ */
+tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float* sa, const int8_t* q,
+                                     int64_t ldq, const float* w_scales, int64_t m, int64_t n, int64_t k,
+                                     void* c, tp_dtype c_dtype, int64_t ldc, int32_t* acc_out,
+                                     int64_t ld_acc, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char* tp_status_string(tp_status status);

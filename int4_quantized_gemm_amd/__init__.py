@@ -13,6 +13,7 @@ of the computation runs in the library's HIP kernels; there is no CPU path.
     tp_qgemm_w4(a, q, s, rotate, out_dtype)    -> C
     tp_qgemm_w8a8(a, q, s, rotate, out_dtype, want_codes, want_acc)
                                                -> C (and qa, sa, acc on request)
+    tp_qgemm_w8a8_prequantized(qa, sa, q, s)   -> C (codes from tp_quantize_rows_int8)
 """
 
 import torch
@@ -175,4 +176,23 @@ def tp_qgemm_w8a8(a, q, scales, rotate=True, out_dtype=torch.float32, out=None, 
                                          _ptr(ws), ws_bytes, _stream(stream)))
     if want_codes or want_acc:
         return out, qa, sa, acc
+    return out
+
+
+def tp_qgemm_w8a8_prequantized(qa, sa, q, scales, out_dtype=torch.float32, out=None, acc=None, stream=None):
+    """C = (float(qa . q^T) * sa[m]) * s[n] on activation codes already made by
+    tp_quantize_rows_int8; optionally also writes the int32 accumulators."""
+    ldqa = _mat(qa, "qa")
+    m, k = qa.shape
+    n = q.shape[0]
+    ldq = _mat(q, "q")
+    _vec(sa, "sa", m)
+    _vec(scales, "w_scales", n)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=qa.device)
+    ldc = _mat(out, "out")
+    ld_acc = _mat(acc, "acc") if acc is not None else 0
+    _lib.check(_lib.load().tp_qgemm_w8a8_prequantized(qa.data_ptr(), ldqa, sa.data_ptr(), q.data_ptr(), ldq,
+                                                      scales.data_ptr(), m, n, k, out.data_ptr(), _dt(out), ldc,
+                                                      _ptr(acc), ld_acc, _stream(stream)))
     return out

@@ -45,6 +45,8 @@ SIGNATURES = {
     "tp_qgemm_w4": (_int, [_p, _int, _i64, _int, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _sz, _p]),
     "tp_qgemm_w8a8": (_int, [_p, _int, _i64, _int, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64,
                               _p, _p, _p, _i64, _p, _sz, _p]),
+    "tp_qgemm_w8a8_prequantized": (_int, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _i64,
+                                           _p]),
     "tp_status_string": (ctypes.c_char_p, [_int]),
     "tp_last_error_message": (ctypes.c_char_p, []),
     "tp_abi_version": (_int, []),

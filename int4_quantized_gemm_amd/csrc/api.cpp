@@ -57,29 +57,38 @@ bool overlaps(const Extent& a, const Extent& b) { return a.lo < b.hi && b.lo < a
 int64_t dtype_size(tp_dtype d) { return d == TP_BF16 ? 2 : 4; }
 bool dtype_ok(int d) { return d == TP_F32 || d == TP_BF16; }
 
-// Validate one row-major operand: non-null, ld >= row length, pitch and base
-// 16-byte aligned, total extent representable. On success stores the extent.
+// Validate one row-major operand: non-null (unless it is empty), ld >= row
+// length, base and pitch aligned to `align` bytes, total extent representable.
+// On success stores the extent (empty for an empty operand).
 tp_status check_matrix(const char* name, const void* p, int64_t rows, int64_t cols_bytes, int64_t ld,
-                       int64_t elem_bytes, Extent* ext) {
-  if (!p) return fail(TP_ERR_NULL_POINTER, "%s is NULL", name);
+                       int64_t elem_bytes, Extent* ext, int64_t align = 16) {
   int64_t pitch;
   if (!mul_ok(ld, elem_bytes, &pitch)) return fail(TP_ERR_SIZE_OVERFLOW, "%s: ld * element size overflows", name);
   if (ld < 0 || pitch < cols_bytes)
     return fail(TP_ERR_BAD_LEADING_DIM, "%s: leading dimension %lld is smaller than the row (%lld bytes)", name,
                 (long long)ld, (long long)cols_bytes);
-  int64_t span;
-  if (rows > 0) {
-    if (!mul_ok(rows - 1, pitch, &span) || !add_ok(span, cols_bytes, &span))
-      return fail(TP_ERR_SIZE_OVERFLOW, "%s: byte extent overflows", name);
+  if (rows == 0 || cols_bytes == 0) {  // empty: nothing is read or written
+    *ext = Extent{};
+    return TP_OK;
   }
-  if (((uintptr_t)p & 15u) != 0) return fail(TP_ERR_MISALIGNED, "%s: base pointer is not 16-byte aligned", name);
-  if (pitch % 16 != 0) return fail(TP_ERR_MISALIGNED, "%s: row pitch of %lld bytes is not a multiple of 16", name,
-                                   (long long)pitch);
+  if (!p) return fail(TP_ERR_NULL_POINTER, "%s is NULL", name);
+  int64_t span;
+  if (!mul_ok(rows - 1, pitch, &span) || !add_ok(span, cols_bytes, &span))
+    return fail(TP_ERR_SIZE_OVERFLOW, "%s: byte extent overflows", name);
+  if (((uintptr_t)p % (uintptr_t)align) != 0)
+    return fail(TP_ERR_MISALIGNED, "%s: base pointer is not %lld-byte aligned", name, (long long)align);
+  if (pitch % align != 0)
+    return fail(TP_ERR_MISALIGNED, "%s: row pitch of %lld bytes is not a multiple of %lld", name, (long long)pitch,
+                (long long)align);
   *ext = extent_of(p, rows, pitch, cols_bytes);
   return TP_OK;
 }
 
 tp_status check_vector(const char* name, const void* p, int64_t count, Extent* ext) {
+  if (count == 0) {
+    *ext = Extent{};
+    return TP_OK;
+  }
   if (!p) return fail(TP_ERR_NULL_POINTER, "%s is NULL", name);
   if (((uintptr_t)p & 3u) != 0) return fail(TP_ERR_MISALIGNED, "%s: not 4-byte aligned", name);
   int64_t bytes;
@@ -235,7 +244,7 @@ tp_status weight_only(int kind, const void* a, tp_dtype a_dtype, int64_t lda, in
   int64_t ns;
   if (!mul_ok(n, kind == tp::GEMM_W8 ? 1 : k / 256, &ns)) return fail(TP_ERR_SIZE_OVERFLOW, "scale count overflows");
   TP_TRY(check_vector("w_scales", w_scales, ns, &es));
-  TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec));
+  TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec, dtype_size(c_dtype)));
   int64_t need;
   if (!workspace_bytes_for(op, m, k, a_flags, &need)) return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
   if (need > 0) {
@@ -307,11 +316,11 @@ tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flag
   TP_TRY(check_matrix("a", a, m, k * dtype_size(a_dtype), lda, dtype_size(a_dtype), &ea));
   TP_TRY(check_matrix("q", q, n, k, ldq, 1, &eq));
   TP_TRY(check_vector("w_scales", w_scales, n, &es));
-  TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec));
+  TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec, dtype_size(c_dtype)));
   const bool own_codes = qa_out && sa_out;
   if (qa_out) TP_TRY(check_matrix("qa_out", qa_out, m, k, k, 1, &eqa));
   if (sa_out) TP_TRY(check_vector("sa_out", sa_out, m, &esa));
-  if (acc_out) TP_TRY(check_matrix("acc_out", acc_out, m, n * 4, ld_acc, 4, &eacc));
+  if (acc_out) TP_TRY(check_matrix("acc_out", acc_out, m, n * 4, ld_acc, 4, &eacc, 4));
   int64_t need = 0;
   if (!own_codes) {
     if (!workspace_bytes_for(TP_OP_QGEMM_W8A8, m, k, a_flags, &need))
@@ -357,4 +366,45 @@ tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flag
   return hip_status(tp::launch_qgemm(g, stream), "product launch");
 }
 
+tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float* sa, const int8_t* q, int64_t ldq,
+                                     const float* w_scales, int64_t m, int64_t n, int64_t k, void* c,
+                                     tp_dtype c_dtype, int64_t ldc, int32_t* acc_out, int64_t ld_acc,
+                                     hipStream_t stream) {
+  if (!dtype_ok(c_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "c_dtype %d is not TP_F32 or TP_BF16", (int)c_dtype);
+  TP_TRY(check_sizes(m, n, k));
+  if (k > INT32_MAX / (127 * 127))
+    return fail(TP_ERR_BAD_SHAPE, "k=%lld: the int32 accumulator could overflow (k <= %d)", (long long)k,
+                INT32_MAX / (127 * 127));
+  Extent eqa, esa, eq, es, ec, eacc;
+  TP_TRY(check_matrix("qa", qa, m, k, ldqa, 1, &eqa));
+  TP_TRY(check_vector("sa", sa, m, &esa));
+  TP_TRY(check_matrix("q", q, n, k, ldq, 1, &eq));
+  TP_TRY(check_vector("w_scales", w_scales, n, &es));
+  TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec, dtype_size(c_dtype)));
+  if (acc_out) TP_TRY(check_matrix("acc_out", acc_out, m, n * 4, ld_acc, 4, &eacc, 4));
+  const Extent* ins[] = {&eqa, &esa, &eq, &es};
+  for (const Extent* i : ins)
+    if (overlaps(ec, *i) || overlaps(eacc, *i)) return fail(TP_ERR_BAD_ALIASING, "an output overlaps an input");
+  if (overlaps(ec, eacc)) return fail(TP_ERR_BAD_ALIASING, "c and acc_out overlap");
+  if (m == 0 || n == 0) return ok();
+  tp::GemmArgs g{};
+  g.kind = tp::GEMM_W8A8;
+  g.a = qa;
+  g.lda = ldqa;
+  g.b = q;
+  g.ldb = ldq;
+  g.w_scales = w_scales;
+  g.a_scales = sa;
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  g.c = c;
+  g.c_bf16 = c_dtype == TP_BF16;
+  g.ldc = ldc;
+  g.acc_out = acc_out;
+  g.ld_acc = ld_acc;
+  return hip_status(tp::launch_qgemm(g, stream), "product launch");
+}
+
 }  // extern "C"
+

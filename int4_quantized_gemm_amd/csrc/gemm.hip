@@ -86,9 +86,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_qgemm(
   // bytes of one B row that one stage reads from global memory
   constexpr int BG = (KIND == GEMM_W8A8) ? 128 : (KIND == GEMM_W8) ? 64 : 32;
   constexpr int B_CPR = BG / 16;  // 16-byte chunks per B row per stage
-  constexpr int A_PER_T = BM * 8 / NT;
-  constexpr int B_PER_T = BN * B_CPR / NT;
-  static_assert(BM * 8 % NT == 0 && BN * B_CPR % NT == 0, "tile does not split evenly over the threads");
+  // 16-byte chunks per thread and stage; when a tile has fewer chunks than
+  // threads, the surplus threads load nothing.
+  constexpr int A_CHUNKS = BM * 8, B_CHUNKS = BN * B_CPR;
+  constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
+  constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
+  constexpr bool A_EVEN = A_CHUNKS % NT == 0, B_EVEN = B_CHUNKS % NT == 0;
   constexpr int A_BUF = BM * LDS_ROW, B_BUF = BN * LDS_ROW;
 
   __shared__ __align__(16) uint8_t smem[2 * (A_BUF + B_BUF)];
@@ -106,7 +109,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_qgemm(
   int a_lds[A_PER_T];
 #pragma unroll
   for (int i = 0; i < A_PER_T; ++i) {
-    const int c = tid + i * NT, row = c >> 3, col = c & 7;
+    const int c = A_EVEN ? tid + i * NT : min(tid + i * NT, A_CHUNKS - 1), row = c >> 3, col = c & 7;
     a_src[i] = A + (int64_t)min(m0 + row, M - 1) * lda_bytes + col * 16;
     a_lds[i] = row * LDS_ROW + col * 16;
   }
@@ -114,7 +117,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_qgemm(
   int b_lds[B_PER_T];
 #pragma unroll
   for (int i = 0; i < B_PER_T; ++i) {
-    const int c = tid + i * NT, row = c / B_CPR, col = c % B_CPR;
+    const int c = B_EVEN ? tid + i * NT : min(tid + i * NT, B_CHUNKS - 1), row = c / B_CPR, col = c % B_CPR;
     b_src[i] = B + (int64_t)min(n0 + row, N - 1) * ldb_bytes + col * 16;
     b_lds[i] = row * LDS_ROW + col * (128 / B_CPR);
   }
@@ -130,9 +133,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_qgemm(
     uint8_t* as = As + buf * A_BUF;
     uint8_t* bs = Bs + buf * B_BUF;
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) *reinterpret_cast<u32x4_t*>(as + a_lds[i]) = ra[i];
+    for (int i = 0; i < A_PER_T; ++i)
+      if (A_EVEN || tid + i * NT < A_CHUNKS) *reinterpret_cast<u32x4_t*>(as + a_lds[i]) = ra[i];
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
+      if (!B_EVEN && tid + i * NT >= B_CHUNKS) continue;
       if constexpr (KIND == GEMM_W8A8) {
         *reinterpret_cast<u32x4_t*>(bs + b_lds[i]) = rb[i];
       } else if constexpr (KIND == GEMM_W8) {
@@ -277,17 +282,42 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Tile table. Wide outputs (many tiles even at 256x256) use 256x256 blocks of
+// 8 waves (128x64 each), which halve the LDS traffic per MAC of a 128x128
+// block; smaller outputs keep 128x128 blocks so that the 256 CUs get several
+// waves of tiles. Chosen from measured sweeps on MI355X.
+enum TileCfg { TILE_128_W64x64 = 0, TILE_256_W128x64 = 1, TILE_128_W32x64 = 2 };
+
+static int pick_tile(int kind, int64_t m, int64_t n, int64_t k) {
+  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  if (kind == GEMM_W4) return TILE_128_W32x64;
+  if (big_tiles >= 768) return TILE_256_W128x64;
+  if (kind == GEMM_W8A8 && k >= 8192) return TILE_128_W64x64;
+  return TILE_128_W32x64;
+}
+
 void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn) {
-  (void)kind; (void)m; (void)n; (void)k;
-  *bm = 128;
-  *bn = 128;
+  const int t = pick_tile(kind, m, n, k);
+  *bm = *bn = (t == TILE_256_W128x64) ? 256 : 128;
+}
+
+template <int KIND>
+static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
+  switch (pick_tile(KIND, g.m, g.n, g.k)) {
+    case TILE_256_W128x64:
+      if constexpr (KIND != GEMM_W4) return launch_tile<KIND, 256, 256, 128, 64>(g, stream);
+      break;
+    case TILE_128_W64x64: return launch_tile<KIND, 128, 128, 64, 64>(g, stream);
+    default: break;
+  }
+  return launch_tile<KIND, 128, 128, 32, 64>(g, stream);
 }
 
 hipError_t launch_qgemm(const GemmArgs& g, hipStream_t stream) {
   switch (g.kind) {
-    case GEMM_W8: return launch_tile<GEMM_W8, 128, 128, 64, 64>(g, stream);
-    case GEMM_W4: return launch_tile<GEMM_W4, 128, 128, 64, 64>(g, stream);
-    case GEMM_W8A8: return launch_tile<GEMM_W8A8, 128, 128, 64, 64>(g, stream);
+    case GEMM_W8: return launch_kind<GEMM_W8>(g, stream);
+    case GEMM_W4: return launch_kind<GEMM_W4>(g, stream);
+    case GEMM_W8A8: return launch_kind<GEMM_W8A8>(g, stream);
   }
   return hipErrorInvalidValue;
 }
