@@ -9,6 +9,20 @@
 
 namespace tp {
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding and leaves the other counters unconstrained
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+#define VMCNT_ENCODE(n) ((((n) & 0xF) | ((((n) >> 4) & 3) << 14)) | 0x0F70)
+
+// s_waitcnt immediate for "all of this wave's LDS operations have completed"
+// (lgkmcnt 0, other counters unconstrained).
+#define LGKMCNT0_ENCODE 0xC07F
+
+// Workgroup barrier without the memory fence of __syncthreads(): waves wait
+// for each other, and the compiler may not move memory operations across it,
+// but no outstanding-memory wait is implied (callers wait explicitly).
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;

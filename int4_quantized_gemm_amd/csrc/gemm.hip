@@ -22,6 +22,7 @@
 #include <type_traits>
 
 #include "device_common.hpp"
+#include "gemm_pp.hpp"
 #include "kernels.hpp"
 
 namespace tp {
@@ -282,32 +283,40 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile table. Wide outputs (many tiles even at 256x256) use 256x256 blocks of
-// 8 waves (128x64 each), which halve the LDS traffic per MAC of a 128x128
-// block; smaller outputs keep 128x128 blocks so that the 256 CUs get several
-// waves of tiles. Chosen from measured sweeps on MI355X.
-enum TileCfg { TILE_128_W64x64 = 0, TILE_256_W128x64 = 1, TILE_128_W32x64 = 2 };
+// Kernel table. Outputs with at least 128 tiles of 256x256 (every
+// diffusion-block projection at M = 4096) run the two-group multi-stage kernel
+// of gemm_pp.hpp: 256x256 tiles of 8 waves (128x64 each) for W8 and W8A8,
+// 256x128 tiles (128x32 each) for W4, whose per-group fold needs a second set
+// of accumulators. Smaller outputs use the single-stage kernels above with
+// 128x128 tiles, so that the 256 CUs still get several tiles each. Chosen from
+// measured sweeps on MI355X.
+enum KernelCfg { CFG_SMALL_128 = 0, CFG_PP_256x256 = 1, CFG_PP_256x128 = 2 };
 
-static int pick_tile(int kind, int64_t m, int64_t n, int64_t k) {
-  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  if (kind == GEMM_W4) return TILE_128_W32x64;
-  if (big_tiles >= 768) return TILE_256_W128x64;
-  if (kind == GEMM_W8A8 && k >= 8192) return TILE_128_W64x64;
-  return TILE_128_W32x64;
+static int pick_cfg(int kind, int64_t m, int64_t n, int64_t k) {
+  (void)k;
+  const int64_t big = ((m + 255) / 256) * ((n + 255) / 256);
+  if (big < 128) return CFG_SMALL_128;
+  return kind == GEMM_W4 ? CFG_PP_256x128 : CFG_PP_256x256;
 }
 
 void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn) {
-  const int t = pick_tile(kind, m, n, k);
-  *bm = *bn = (t == TILE_256_W128x64) ? 256 : 128;
+  switch (pick_cfg(kind, m, n, k)) {
+    case CFG_PP_256x256: *bm = 256; *bn = 256; return;
+    case CFG_PP_256x128: *bm = 256; *bn = 128; return;
+    default: *bm = 128; *bn = 128; return;
+  }
 }
 
 template <int KIND>
 static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
-  switch (pick_tile(KIND, g.m, g.n, g.k)) {
-    case TILE_256_W128x64:
-      if constexpr (KIND != GEMM_W4) return launch_tile<KIND, 256, 256, 128, 64>(g, stream);
+  switch (pick_cfg(KIND, g.m, g.n, g.k)) {
+    case CFG_PP_256x256:
+      if constexpr (KIND == GEMM_W8A8) return launch_pp<KIND, 256, 256, 128, 64, 4>(g, stream);
+      if constexpr (KIND == GEMM_W8) return launch_pp<KIND, 256, 256, 128, 64, 3>(g, stream);
       break;
-    case TILE_128_W64x64: return launch_tile<KIND, 128, 128, 64, 64>(g, stream);
+    case CFG_PP_256x128:
+      if constexpr (KIND == GEMM_W4) return launch_pp<KIND, 256, 128, 128, 32, 3>(g, stream);
+      break;
     default: break;
   }
   return launch_tile<KIND, 128, 128, 32, 64>(g, stream);

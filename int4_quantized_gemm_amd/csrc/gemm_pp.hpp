@@ -1,0 +1,401 @@
+// Quantized products on the gfx950 matrix cores: two-group ("ping-pong")
+// schedule over a multi-stage LDS ring.
+//
+//   W8    C = (bf16(A') . q^T) * s[n]              bf16 MFMA 16x16x32, fp32 sums
+//   W4    C = sum_g s[n,g] * (bf16(A'_g) . q_g^T)  bf16 MFMA, per-group fp32 fold
+//   W8A8  acc = qa . q^T (int32, exact); C = (float(acc) * sa[m]) * sw[n]
+//                                                   i8 MFMA 16x16x64, int32 sums
+//
+// (tensai docs, "画像生成", section "幅とメモリ": int8 weights with one scale per
+// row and the 4-bit "-q4" width; section "GPU": activations quantized on the
+// device. TensorFold pull request #948: bf16 activations, fp32 sums.)
+//
+// Schedule. A block of 8 waves (two per SIMD) computes a BM x BN tile; the
+// waves form two groups of four, one wave of each group per SIMD. K advances
+// in stages of 64 elements through an LDS ring of NSTAGE stages filled with
+// global_load_lds_dwordx4 (no register staging). Each stage is two half-steps
+// separated by barriers; in every half-step one group runs its memory phase
+// (read the stage's operand fragments from LDS into registers, issue the
+// direct loads of stage k + NSTAGE - 1) while the other runs its compute phase
+// (back-to-back MFMAs on fragments already in registers). Group 1 trails group
+// 0 by one half-step, so on every SIMD one wave feeds the matrix unit while
+// the other waits on LDS. Stage k is read by group 0 in half-step 2k and by
+// group 1 in half-step 2k+1; its buffer is refilled (with stage k + NSTAGE)
+// only from half-step 2k+2 on.
+//
+// LDS layouts (per stage; 16-byte granules; every wave-level direct load fills
+// 1 KB, lane p writing granule p, so the swizzle is applied by choosing which
+// global granule each lane loads). A fragment read has 16 lanes read the same
+// logical chunk of 16 consecutive rows; with 64 banks of 4 bytes, the swizzles
+// below put those 16 reads in 16 distinct bank groups:
+//   int8 rows of 64 B (A of W8A8, B of W8A8 and W8): granule c of row r at
+//     c ^ ((r >> 2) & 3);
+//   bf16 rows of 128 B (A of W8, W4): granule c of row r at c ^ ((r >> 1) & 7);
+//   int4 rows of 32 B (B of W4, read 8 bytes at a time): granule c of row r at
+//     c ^ ((r >> 3) & 1).
+// K order inside a stage: MFMA k-step kk (0, 1) of the bf16 kinds gives lane
+// group g = lane/16 the K positions 16g + 8kk + [0, 8); A and B use the same
+// order, so one 16-byte int8 (8-byte int4) weight read serves both k-steps.
+// The i8 kind has one k-step per stage: 16g + [0, 16).
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace tp {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Block -> tile map: each of the 8 XCDs owns one contiguous range of logical
+// tiles (hardware deals blocks round-robin over XCDs), walked in groups of 8
+// tile-rows so that blocks resident together on one XCD share A rows and B
+// columns in that XCD's L2.
+__device__ __forceinline__ void pp_map_tile(int pid, int nblk, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int q = nblk >> 3, r = nblk & 7;
+  const int xcd = pid & 7, idx = pid >> 3;
+  const int logical = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  constexpr int GM = 8;
+  const int width = GM * tiles_n;
+  const int group = logical / width;
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int within = logical - group * width;
+  tm = first_m + within % gsize;
+  tn = within / gsize;
+}
+
+// 8 int8 codes (two dwords) -> 8 bf16 (four dwords), exact.
+__device__ __forceinline__ bf16x8_t pp_widen_i8x8(uint32_t lo, uint32_t hi) {
+  u32x4_t o;
+  o.x = pack_bf16x2((float)(int8_t)(lo), (float)(int8_t)(lo >> 8));
+  o.y = pack_bf16x2((float)(int8_t)(lo >> 16), (float)(int8_t)(lo >> 24));
+  o.z = pack_bf16x2((float)(int8_t)(hi), (float)(int8_t)(hi >> 8));
+  o.w = pack_bf16x2((float)(int8_t)(hi >> 16), (float)(int8_t)(hi >> 24));
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
+// 8 int4 codes (one dword, code j in bits 4j..4j+3) -> 8 bf16, exact.
+__device__ __forceinline__ bf16x8_t pp_widen_i4x8(uint32_t w) {
+  const int32_t v = (int32_t)w;
+  u32x4_t o;
+  o.x = pack_bf16x2((float)((v << 28) >> 28), (float)((v << 24) >> 28));
+  o.y = pack_bf16x2((float)((v << 20) >> 28), (float)((v << 16) >> 28));
+  o.z = pack_bf16x2((float)((v << 12) >> 28), (float)((v << 8) >> 28));
+  o.w = pack_bf16x2((float)((v << 4) >> 28), (float)(v >> 28));
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE>
+struct PPCfg {
+  static constexpr bool I8 = KIND == GEMM_W8A8;
+  static constexpr int NW = 8, NT = 512;
+  static constexpr int NWN = BN / WN;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  static constexpr int AROW = I8 ? 64 : 128;              // A bytes per row per stage
+  static constexpr int BROW = KIND == GEMM_W4 ? 32 : 64;  // B bytes per row per stage
+  static constexpr int A_STAGE = BM * AROW, B_STAGE = BN * BROW, STAGE = A_STAGE + B_STAGE;
+  static constexpr int A_LOADS = A_STAGE / 1024, LOADS = (A_STAGE + B_STAGE) / 1024;
+  static constexpr int HALF = (LOADS + 1) / 2;            // loads owned by each group per stage
+  static constexpr int LPW = (HALF + 3) / 4;              // loads per wave per stage
+  static constexpr int LDS_BYTES = NSTAGE * STAGE;
+  static_assert((BM / WM) * (BN / WN) == NW, "the tile must split into 8 waves");
+  static_assert(A_STAGE % 1024 == 0 && B_STAGE % 1024 == 0, "a stage must be whole 1 KB loads");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
+  static_assert(NSTAGE >= 3, "the two-group schedule needs at least three stages");
+  static_assert(LPW * (NSTAGE - 2) < 64, "vmcnt range");
+};
+
+template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE, bool OUT_BF16, bool ACC_OUT>
+__global__ __launch_bounds__(512, 1) void k_qgemm_pp(
+    const uint8_t* __restrict__ A, int64_t lda_bytes, const uint8_t* __restrict__ B, int64_t ldb_bytes,
+    const float* __restrict__ sw, const float* __restrict__ sa, int M, int N, int K, void* __restrict__ Cv,
+    int64_t ldc, int32_t* __restrict__ acc_out, int64_t ld_acc, int tiles_m, int tiles_n) {
+  using Cfg = PPCfg<KIND, BM, BN, WM, WN, NSTAGE>;
+  constexpr bool I8 = Cfg::I8;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, NWN = Cfg::NWN;
+  constexpr int AROW = Cfg::AROW, BROW = Cfg::BROW, STAGE = Cfg::STAGE, A_STAGE = Cfg::A_STAGE;
+  constexpr int LOADS = Cfg::LOADS, A_LOADS = Cfg::A_LOADS, HALF = Cfg::HALF, LPW = Cfg::LPW;
+
+  __shared__ __align__(1024) uint8_t ring[Cfg::LDS_BYTES];
+
+  int tm, tn;
+  pp_map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;  // waves 0-3: group 0, 4-7: group 1 (one of each per SIMD)
+  const int wm0 = (wave / NWN) * WM, wn0 = (wave % NWN) * WN;
+
+  // Direct-load slots of this wave: group g owns loads [g*HALF, g*HALF + HALF)
+  // of each stage; surplus slots repeat the group's last load (same bytes to
+  // the same place).
+  const uint8_t* src[LPW];
+  int dst[LPW];
+  int kbytes[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int lim = min(grp * HALF + HALF, LOADS) - 1;
+    const int L = min(grp * HALF + (wave & 3) * LPW + i, lim);
+    if (L < A_LOADS) {
+      if constexpr (I8) {  // 16 rows x 64 B
+        const int row = L * 16 + (lane >> 2), c = (lane & 3) ^ ((row >> 2) & 3);
+        src[i] = A + (int64_t)min(m0 + row, M - 1) * lda_bytes + c * 16;
+      } else {  // 8 rows x 128 B
+        const int row = L * 8 + (lane >> 3), c = (lane & 7) ^ ((row >> 1) & 7);
+        src[i] = A + (int64_t)min(m0 + row, M - 1) * lda_bytes + c * 16;
+      }
+      dst[i] = L * 1024;
+      kbytes[i] = AROW;
+    } else {
+      const int LB = L - A_LOADS;
+      if constexpr (KIND == GEMM_W4) {  // 32 rows x 32 B
+        const int row = LB * 32 + (lane >> 1), c = (lane & 1) ^ ((row >> 3) & 1);
+        src[i] = B + (int64_t)min(n0 + row, N - 1) * ldb_bytes + c * 16;
+      } else {  // 16 rows x 64 B
+        const int row = LB * 16 + (lane >> 2), c = (lane & 3) ^ ((row >> 2) & 3);
+        src[i] = B + (int64_t)min(n0 + row, N - 1) * ldb_bytes + c * 16;
+      }
+      dst[i] = A_STAGE + LB * 1024;
+      kbytes[i] = BROW;
+    }
+  }
+  const int KS = K >> 6;  // stages of 64 K
+  auto issue_stage = [&](int ks) {
+    uint8_t* base = ring + (ks % NSTAGE) * STAGE;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + (int64_t)ks * kbytes[i]), (lds_void_t*)(base + dst[i]),
+                                       16, 0, 0);
+  };
+
+  typedef typename std::conditional<I8, i32x4_t, f32x4_t>::type acc_t;
+  acc_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+  f32x4_t tot[KIND == GEMM_W4 ? FM : 1][KIND == GEMM_W4 ? FN : 1];
+  if constexpr (KIND == GEMM_W4) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) tot[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int groups = K >> 8;
+
+  // Fragments of one stage, held in registers between the memory phase and
+  // the compute phase.
+  constexpr int NKK = I8 ? 1 : 2;
+  u32x4_t fa[NKK][FM];
+  typedef typename std::conditional<KIND == GEMM_W4, uint2, u32x4_t>::type braw_t;
+  braw_t fb[FN];
+  float s_grp[KIND == GEMM_W4 ? FN : 1];  // W4: scales of the group being folded
+
+  auto mem_phase = [&](int ks) {
+    const uint8_t* as = ring + (ks % NSTAGE) * STAGE;
+    const uint8_t* bs = as + A_STAGE;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn0 + j * 16 + r16;
+      if constexpr (KIND == GEMM_W4)
+        fb[j] = *reinterpret_cast<const uint2*>(bs + row * 32 + ((((g4 >> 1) ^ ((row >> 3) & 1)) << 4) | ((g4 & 1) << 3)));
+      else
+        fb[j] = *reinterpret_cast<const u32x4_t*>(bs + row * 64 + ((g4 ^ ((row >> 2) & 3)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm0 + i * 16 + r16;
+      if constexpr (I8) {
+        fa[0][i] = *reinterpret_cast<const u32x4_t*>(as + row * 64 + ((g4 ^ ((row >> 2) & 3)) << 4));
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          fa[kk][i] = *reinterpret_cast<const u32x4_t*>(as + row * 128 + (((2 * g4 + kk) ^ ((row >> 1) & 7)) << 4));
+      }
+    }
+    if constexpr (KIND == GEMM_W4) {
+      if ((ks & 3) == 3) {  // last stage of a 256-group: fetch the group's scales for the fold
+        const int g = ks >> 2;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = min(n0 + wn0 + j * 16 + r16, N - 1);
+          s_grp[j] = sw[(int64_t)col * groups + g];
+        }
+      }
+    }
+    if (ks + NSTAGE - 1 < KS) issue_stage(ks + NSTAGE - 1);
+  };
+
+  auto compute_phase = [&](int ks) {
+    if constexpr (I8) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, fa[0][i]),
+                                                             __builtin_bit_cast(i32x4_t, fb[j]), acc[i][j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        bf16x8_t b0, b1;
+        if constexpr (KIND == GEMM_W4) {
+          b0 = pp_widen_i4x8(fb[j].x);
+          b1 = pp_widen_i4x8(fb[j].y);
+        } else {
+          b0 = pp_widen_i8x8(fb[j].x, fb[j].y);
+          b1 = pp_widen_i8x8(fb[j].z, fb[j].w);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[0][i]), b0, acc[i][j],
+                                                               0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[1][i]), b1, acc[i][j],
+                                                               0, 0, 0);
+      }
+    }
+    if constexpr (KIND == GEMM_W4) {
+      if ((ks & 3) == 3) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            tot[i][j] += s_grp[j] * acc[i][j];
+            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+    }
+  };
+
+  // Epilogue scales, fetched before the main loop: their latency is hidden by
+  // the loop, and no load is left to interleave with the output stores (on
+  // gfx9 loads and stores share one completion counter, so a load waited on
+  // between stores would drain every store before it).
+  float ep_sw[KIND == GEMM_W4 ? 1 : FN];
+  float ep_sa[KIND == GEMM_W8A8 ? FM : 1][4];
+  if constexpr (KIND != GEMM_W4) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) ep_sw[j] = sw[min(n0 + wn0 + j * 16 + r16, N - 1)];
+  }
+  if constexpr (KIND == GEMM_W8A8) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ep_sa[i][r] = sa[min(m0 + wm0 + i * 16 + g4 * 4 + r, M - 1)];
+  }
+
+  // Stage ks+1 has landed once at most the loads of stages ks+2 .. ks+NSTAGE-1
+  // (issued after it by this wave) are outstanding.
+  auto wait_next = [&](int ks) {
+    if (ks + 1 >= KS) return;
+    if (ks + NSTAGE - 1 < KS) {
+      __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(LPW * (NSTAGE - 2)));
+    } else {
+      __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(0));
+    }
+  };
+
+  // Prologue: stages 0 .. NSTAGE-2 in flight, stage 0 landed everywhere.
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < KS) issue_stage(s);
+  if (NSTAGE - 2 < KS) {
+    __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(LPW * (NSTAGE - 2)));
+  } else {
+    __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(0));
+  }
+  barrier_only();
+
+  // Both groups run the same body (memory phase, barrier, compute phase,
+  // barrier); group 1 starts one barrier later and group 0 ends one barrier
+  // later, so in every half-step the groups are in opposite phases. Barrier
+  // 2ks+1 separates group 0's M(ks) from its C(ks) and group 1's C(ks-1) from
+  // its M(ks); stage ks+1 must have landed (in both groups' halves) before
+  // barrier 2ks+2, after which group 0 reads it.
+  if (grp == 1) barrier_only();
+  for (int ks = 0; ks < KS; ++ks) {
+    mem_phase(ks);
+    if (grp == 1) wait_next(ks);
+    // The LDS reads of the memory phase must be complete before any wave can
+    // pass the barrier and refill the buffer they read.
+    __builtin_amdgcn_s_waitcnt(LGKMCNT0_ENCODE);
+    barrier_only();
+    compute_phase(ks);
+    if (grp == 0) wait_next(ks);
+    barrier_only();
+  }
+  if (grp == 0) barrier_only();
+
+  // Epilogue: lane l of a 16x16 tile holds rows 4*(l/16)+r, column l%16.
+  // Every load this wave issued has completed here; waiting once up front
+  // keeps the compiler from re-waiting on the preloaded scales between
+  // stores. Interior tiles store without bounds checks.
+  __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(0));
+  auto value = [&](int i, int j, int r) -> float {
+    if constexpr (KIND == GEMM_W8A8) {
+      return ((float)acc[i][j][r] * ep_sa[i][r]) * ep_sw[j];
+    } else if constexpr (KIND == GEMM_W8) {
+      return acc[i][j][r] * ep_sw[j];
+    } else {
+      return tot[i][j][r];
+    }
+  };
+  typedef typename std::conditional<OUT_BF16, __bf16, float>::type out_t;
+  const int row0 = m0 + wm0 + g4 * 4, col0 = n0 + wn0 + r16;
+  out_t* cbase = reinterpret_cast<out_t*>(Cv) + (int64_t)row0 * ldc + col0;
+  int32_t* abase = ACC_OUT ? acc_out + (int64_t)row0 * ld_acc + col0 : nullptr;
+  if ((m0 + BM <= M) && (n0 + BN <= N)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        out_t* crow = cbase + (int64_t)(i * 16 + r) * ldc;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          crow[j * 16] = (out_t)value(i, j, r);
+          if constexpr (ACC_OUT) abase[(int64_t)(i * 16 + r) * ld_acc + j * 16] = acc[i][j][r];
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (row0 + i * 16 + r >= M) continue;
+        out_t* crow = cbase + (int64_t)(i * 16 + r) * ldc;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (col0 + j * 16 >= N) continue;
+          crow[j * 16] = (out_t)value(i, j, r);
+          if constexpr (ACC_OUT) abase[(int64_t)(i * 16 + r) * ld_acc + j * 16] = acc[i][j][r];
+        }
+      }
+  }
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE>
+static hipError_t launch_pp(const GemmArgs& g, hipStream_t stream) {
+  const int tiles_m = (int)((g.m + BM - 1) / BM), tiles_n = (int)((g.n + BN - 1) / BN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(512);
+  const int64_t lda_bytes = g.lda * (KIND == GEMM_W8A8 ? 1 : 2);
+  const uint8_t* a = (const uint8_t*)g.a;
+  const uint8_t* b = (const uint8_t*)g.b;
+#define TP_LAUNCH_PP(OB, AO)                                                                                   \
+  hipLaunchKernelGGL((k_qgemm_pp<KIND, BM, BN, WM, WN, NSTAGE, OB, AO>), grid, block, 0, stream, a, lda_bytes, b, \
+                     g.ldb, g.w_scales, g.a_scales, (int)g.m, (int)g.n, (int)g.k, g.c, g.ldc, g.acc_out, g.ld_acc, \
+                     tiles_m, tiles_n)
+  if (KIND == GEMM_W8A8 && g.acc_out) {
+    if (g.c_bf16) TP_LAUNCH_PP(true, true); else TP_LAUNCH_PP(false, true);
+  } else {
+    if (g.c_bf16) TP_LAUNCH_PP(true, false); else TP_LAUNCH_PP(false, false);
+  }
+#undef TP_LAUNCH_PP
+  return hipGetLastError();
+}
+
+}  // namespace tp

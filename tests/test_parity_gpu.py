@@ -28,9 +28,16 @@ pytestmark = pytest.mark.gpu
 
 
 # ------------------------------------------------------------------ helpers
-def _weights_i8(w_cpu, d):
-    q, s = tp.tp_rotate_quantize_weights(w_cpu.to(d), bits=8)
-    return q, s
+_ORACLE_W = {}
+
+
+def oracle_weights(key, w_cpu, bits):
+    """The oracle's own rotated, quantized weights (never the device's)."""
+    k = (key, bits)
+    if k not in _ORACLE_W:
+        wn = w_cpu.float().numpy()
+        _ORACLE_W[k] = oracle.quantize_weights_int8(wn) if bits == 8 else oracle.quantize_weights_int4(wn)
+    return _ORACLE_W[k]
 
 
 def _check_weights(w_cpu, bits, d):
@@ -179,14 +186,15 @@ def test_quantize_rows_zero_and_tiny_rows():
 
 
 # ------------------------------------------------------------- W8 / W4 products
-def _w8_case(wl, rows=None, row_sel=None, out_dtype=None):
+def _w8_case(wl, row_sel=None, out_dtype=None):
     d = dev()
     x, w = W.generate(wl)
     q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
     odt = out_dtype or (torch.float32 if wl.out_dtype == "f32" else torch.bfloat16)
     y = tp.tp_qgemm_w8(x.to(d), q, s, rotate=True, out_dtype=odt)
     sel = row_sel if row_sel is not None else np.arange(wl.m)
-    ref = oracle.qgemm_w8(f64(x)[sel], host(q), host(s))
+    rq, rs = oracle_weights(wl, w, 8)
+    ref = oracle.qgemm_w8(f64(x)[sel], rq, rs)
     return f64(y)[sel], ref
 
 
@@ -197,7 +205,8 @@ def _w4_case(wl, row_sel=None, out_dtype=None):
     odt = out_dtype or (torch.float32 if wl.out_dtype == "f32" else torch.bfloat16)
     y = tp.tp_qgemm_w4(x.to(d), q, s, rotate=True, out_dtype=odt)
     sel = row_sel if row_sel is not None else np.arange(wl.m)
-    ref = oracle.qgemm_w4(f64(x)[sel], host(q), host(s))
+    rq, rs = oracle_weights(wl, w, 4)
+    ref = oracle.qgemm_w4(f64(x)[sel], rq, rs)
     return f64(y)[sel], ref
 
 
@@ -242,10 +251,12 @@ def test_weight_only_ragged(kind, m, n, k):
     announce("tp_qgemm", kind, "ragged", m, n, k)
     wl = W.TINY.with_(m=m, n=n, k=k, seed=m * 7 + n, act_outliers=2, w_outliers=2)
     x, w = W.generate(wl)
-    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8 if kind == "w8" else 4)
+    bits = 8 if kind == "w8" else 4
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=bits)
     fn = tp.tp_qgemm_w8 if kind == "w8" else tp.tp_qgemm_w4
     y = fn(x.to(d), q, s, rotate=True, out_dtype=torch.float32)
-    ref = (oracle.qgemm_w8 if kind == "w8" else oracle.qgemm_w4)(f64(x), host(q), host(s))
+    rq, rs = oracle_weights(wl, w, bits)
+    ref = (oracle.qgemm_w8 if kind == "w8" else oracle.qgemm_w4)(f64(x), rq, rs)
     err = assert_bf16_path(f64(y), ref, f"{kind} ragged")
     assert err < 1e-4
 
@@ -262,7 +273,8 @@ def test_w8_prerotated_padded_views():
     cbuf = torch.full((100, 320 + 64), 7.0, dtype=torch.float32, device=d)
     out = cbuf[3:99, 32:352]
     tp.tp_qgemm_w8(abuf[2:98, 128:1152], q, s, rotate=False, out=out)
-    ref = oracle.qgemm_w8(f64(xr), host(q), host(s), rotate=False)
+    rq, rs = oracle_weights(wl, w, 8)
+    ref = oracle.qgemm_w8(f64(x), rq, rs)   # the oracle rotates the raw input itself
     assert_bf16_path(f64(out), ref, "w8 prerotated view")
     assert torch.all(cbuf[:3] == 7.0) and torch.all(cbuf[99:] == 7.0)
     assert torch.all(cbuf[:, :32] == 7.0) and torch.all(cbuf[:, 352:] == 7.0)
@@ -275,7 +287,8 @@ def _w8a8_case(wl, row_sel=None):
     q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
     y, qa, sa, acc = tp.tp_qgemm_w8a8(x.to(d), q, s, rotate=True, want_codes=True, want_acc=True)
     sel = row_sel if row_sel is not None else np.arange(wl.m)
-    ry, racc, rqa, rsa = oracle.qgemm_w8a8(f64(x)[sel], host(q), host(s))
+    rq, rs = oracle_weights(wl, w, 8)
+    ry, racc, rqa, rsa = oracle.qgemm_w8a8(f64(x)[sel], rq, rs)
     assert np.array_equal(host(sa)[sel], rsa), "activation scales differ"
     assert np.array_equal(host(qa)[sel], rqa), "activation codes differ"
     gacc = host(acc)[sel].astype(np.int64)
@@ -302,6 +315,45 @@ def test_w8a8_dit_block_sampled(name):
 def test_w8a8_ragged(m, n, k):
     announce("tp_qgemm_w8a8 ragged", m, n, k)
     _w8a8_case(W.TINY.with_(m=m, n=n, k=k, seed=m + 3 * n, act_outliers=2, w_outliers=2, path="w8a8"))
+
+
+@pytest.mark.parametrize("kind,m,n,k", [("w8a8", 4000, 9000, 768), ("w8", 4000, 8000, 512),
+                                        ("w4", 4000, 8000, 1024), ("w8a8", 2100, 9000, 256)])
+def test_multistage_path_ragged(kind, m, n, k):
+    """Shapes large enough for the 256-wide multi-stage kernels, with M and N
+    not multiples of the tile: sampled whole rows incl. the last tile row."""
+    wl = W.PROJ256.with_(name=f"ragged_{kind}_{m}_{n}_{k}", m=m, n=n, k=k, seed=m + n + k, path=kind,
+                         out_dtype="f32" if kind == "w8a8" else "bf16")
+    announce("multistage ragged", kind, m, n, k)
+    sel = sample_rows(m, 24, seed=k)
+    if kind == "w8a8":
+        _w8a8_case(wl, row_sel=sel)
+    elif kind == "w8":
+        got, ref = _w8_case(wl, row_sel=sel)
+        assert_bf16_path(got, ref, "w8 multistage ragged")
+    else:
+        got, ref = _w4_case(wl, row_sel=sel)
+        assert_bf16_path(got, ref, "w4 multistage ragged")
+
+
+def test_multistage_padded_views():
+    """Multi-stage W8A8 on a padded, offset activation view and output view."""
+    d = dev()
+    announce("multistage padded views")
+    wl = W.PROJ256.with_(name="padded_views", m=2100, n=9000, k=512, seed=77, path="w8a8", out_dtype="f32")
+    x, w = W.generate(wl)
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    abuf = torch.zeros((wl.m + 3, wl.k + 64), dtype=torch.bfloat16, device=d)
+    abuf[1:1 + wl.m, 32:32 + wl.k] = x.to(d)
+    cbuf = torch.full((wl.m + 2, wl.n + 8), -3.0, dtype=torch.float32, device=d)
+    out = cbuf[1:1 + wl.m, 4:4 + wl.n]
+    tp.tp_qgemm_w8a8(abuf[1:1 + wl.m, 32:32 + wl.k], q, s, out=out)
+    sel = sample_rows(wl.m, 16, seed=3)
+    rq, rs = oracle_weights(wl, w, 8)
+    ry, _, _, _ = oracle.qgemm_w8a8(f64(x)[sel], rq, rs)
+    assert_w8a8_out(f64(out)[sel], ry, "padded views")
+    assert torch.all(cbuf[0] == -3.0) and torch.all(cbuf[-1] == -3.0)
+    assert torch.all(cbuf[:, :4] == -3.0) and torch.all(cbuf[:, 4 + wl.n:] == -3.0)
 
 
 def test_w8a8_planted_integers():
