@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=0,
                    help="activation rows of the CPU oracle sample (0: all rows of every product)")
     p.add_argument("--cpu-only", action="store_true", help="time only the CPU oracle sample (no GPU)")
+    p.add_argument("--small-m", action="store_true",
+                   help="instead of the step: the M <= 64 HBM-bound sweep (one JSON line per case)")
     return p.parse_args()
 
 
@@ -128,6 +130,80 @@ def cpu_baseline(rows):
     }
 
 
+# ------------------------------------------------------- M <= 64 sweep (HBM)
+def small_m_sweep(args):
+    """Products with 1, 16 and 64 activation rows against the full-size
+    weights of the step. They are bound by reading the weights, so each case
+    cycles through enough distinct copies of the packed weight (at least
+    2 x 256 MB) that no launch finds its weight in the 256 MB last-level cache.
+    Bytes per launch = weight codes + scales + activation operand + output."""
+    import torch
+    import int4_quantized_gemm_amd as tp
+    import workloads as W
+
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+    cases = [("w8", W.FFN_UP), ("w4", W.FFN_DOWN), ("w8a8", W.DIT_QKV), ("w8a8", W.DIT_GATEUP)]
+    for kind, wl in cases:
+        _, w = W.generate(wl, rows=1)
+        bits = 4 if kind == "w4" else 8
+        q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=bits)
+        del w
+        wbytes = q.numel() + s.numel() * 4
+        copies = max(2, -(-2 * 256 * 2 ** 20 // wbytes))
+        qs = [(q.clone(), s.clone()) for _ in range(copies)]
+        del q, s
+        for m in (1, 16, 64):
+            x, _ = W.generate(wl.with_(m=m), rows=m)
+            xd = x.to(d)
+            if kind == "w8a8":
+                qa, sa = tp.tp_quantize_rows_int8(xd)
+                out = torch.empty((m, wl.n), dtype=torch.float32, device=d)
+                ws = torch.empty((max(1, tp.tp_workspace_size(4, m, wl.n, wl.k, 0)),), dtype=torch.uint8, device=d)
+                fn = lambda i: tp.tp_qgemm_w8a8_prequantized(qa, sa, qs[i][0], qs[i][1], out=out, workspace=ws)
+                abytes = m * wl.k + m * 4
+            else:
+                xr = tp.tp_hadamard_rotate_rows(xd, out_dtype=torch.bfloat16)
+                out = torch.empty((m, wl.n), dtype=torch.bfloat16, device=d)
+                op = 1 if kind == "w8" else 2
+                ws = torch.empty((max(1, tp.tp_workspace_size(op, m, wl.n, wl.k, 0)),), dtype=torch.uint8, device=d)
+                g = tp.tp_qgemm_w8 if kind == "w8" else tp.tp_qgemm_w4
+                fn = lambda i, g=g: g(xr, qs[i][0], qs[i][1], rotate=False, out=out, workspace=ws)
+                abytes = m * wl.k * 2
+            nbytes = wbytes + abytes + out.numel() * out.element_size()
+            # One graph replays a call on every weight copy: the timing is
+            # then the GPU's, not the Python launch rate's.
+            for i in range(copies):
+                fn(i)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(copies):
+                    fn(i)
+            graph.replay()
+            torch.cuda.synchronize()
+            reps = max(2, -(-64 // copies))
+            med = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                med.append(e0.elapsed_time(e1) / (reps * copies) * 1e-3)
+            del graph
+            t_med, t_min = float(np.median(med)), float(np.min(med))
+            gbs = nbytes / t_med / 1e9
+            print(json.dumps({"metric": "small-M product HBM bandwidth", "case": f"{kind}[{wl.name}]", "m": m,
+                              "n": wl.n, "k": wl.k, "bytes": nbytes, "us_median": round(t_med * 1e6, 2),
+                              "us_min": round(t_min * 1e6, 2), "gbs": round(gbs, 1),
+                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "weight_copies": copies,
+                              "tflops": round(2.0 * m * wl.n * wl.k / t_med / 1e12, 2)}), flush=True)
+        del qs
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ GPU path
 def main():
     args = parse()
@@ -137,6 +213,9 @@ def main():
         sys.exit(2)
     if args.cpu_only:
         print(json.dumps(cpu_baseline(args.cpu_rows)))
+        return
+    if args.small_m:
+        small_m_sweep(args)
         return
 
     import torch
@@ -184,7 +263,7 @@ def main():
                              lambda e=e: tp.tp_quantize_rows_int8(e["x"], qa=e["qa"], sa=e["sa"])))
             launches.append((f"gemm_w8a8[{wl.name}]", "i8", 2.0 * wl.m * wl.n * wl.k,
                              lambda e=e: tp.tp_qgemm_w8a8_prequantized(e["qa"], e["sa"], e["q"], e["s"],
-                                                                       out=e["out"])))
+                                                                       out=e["out"], workspace=ws)))
         else:
             launches.append((f"rotate_bf16[{wl.name}]", "hbm", wl.m * wl.k * (2 + 2),
                              lambda e=e: tp.tp_hadamard_rotate_rows(e["x"], out=e["xr"])))

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 1
+#define TP_ABI_VERSION 2
 
 typedef enum tp_status {
   TP_OK = 0,
@@ -85,7 +85,8 @@ typedef enum tp_dtype {
 typedef enum tp_op {
   TP_OP_QGEMM_W8 = 1,
   TP_OP_QGEMM_W4 = 2,
-  TP_OP_QGEMM_W8A8 = 3
+  TP_OP_QGEMM_W8A8 = 3,
+  TP_OP_QGEMM_W8A8_PREQUANTIZED = 4
 } tp_op;
 
 /*
@@ -148,6 +149,15 @@ tp_status tp_quantize_rows_int8(const void* x, tp_dtype x_dtype, int64_t m, int6
  * tp_workspace_size -- bytes of device workspace the product `op` needs for
  * these sizes and a_flags (0 when none is needed). Returns 0 for invalid
  * sizes as well; the product call itself reports the error.
+ *
+ * The workspace holds, in this order: the rotated bf16 activations (W8, W4
+ * with TP_A_ROTATE: 2 m k bytes) or the activation codes and scales (W8A8
+ * unless the caller takes them through qa_out / sa_out); then, for products
+ * with few rows (m <= 64), the split-K partial sums (4 m n bytes per split;
+ * the split count depends on m, n and k). The size therefore depends on all
+ * of op, m, n, k and a_flags. A product given less than it needs returns
+ * TP_ERR_WORKSPACE_TOO_SMALL; W8A8 with both qa_out and sa_out needs only the
+ * partial-sum part. The contents are scratch: nothing is kept between calls.
  */
 size_t tp_workspace_size(tp_op op, int64_t m, int64_t n, int64_t k, int a_flags);
 
@@ -226,12 +236,15 @@ tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flag
  *   c        [m, n], TP_F32 or TP_BF16, row pitch ldc:
  *            C[r, c] = (float(acc[r, c]) * sa[r]) * w_scales[c].
  *   acc_out  optional int32 [m, n] raw accumulators, row pitch ld_acc.
- *   No workspace. k <= 133144.
+ *   workspace  tp_workspace_size(TP_OP_QGEMM_W8A8_PREQUANTIZED, m, n, k, 0)
+ *            bytes (0, and NULL allowed, unless m is small enough for the
+ *            split-K path). k <= 133144.
  */
 tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float* sa, const int8_t* q,
                                      int64_t ldq, const float* w_scales, int64_t m, int64_t n, int64_t k,
                                      void* c, tp_dtype c_dtype, int64_t ldc, int32_t* acc_out,
-                                     int64_t ld_acc, hipStream_t stream);
+                                     int64_t ld_acc, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char* tp_status_string(tp_status status);

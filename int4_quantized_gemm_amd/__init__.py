@@ -167,7 +167,8 @@ def tp_qgemm_w8a8(a, q, scales, rotate=True, out_dtype=torch.float32, out=None, 
         acc = torch.empty((m, n), dtype=torch.int32, device=a.device)
     flags = TP_A_ROTATE if rotate else TP_A_PREROTATED
     if want_codes:
-        ws, ws_bytes = (None, 0) if workspace is None else (workspace, workspace.numel() * workspace.element_size())
+        # the codes go to qa / sa: only the split-K partial sums need scratch
+        ws, ws_bytes = _workspace(_lib.TP_OP_QGEMM_W8A8_PREQUANTIZED, m, n, k, flags, a.device, workspace)
     else:
         ws, ws_bytes = _workspace(_lib.TP_OP_QGEMM_W8A8, m, n, k, flags, a.device, workspace)
     ld_acc = _mat(acc, "acc") if acc is not None else 0
@@ -179,7 +180,8 @@ def tp_qgemm_w8a8(a, q, scales, rotate=True, out_dtype=torch.float32, out=None, 
     return out
 
 
-def tp_qgemm_w8a8_prequantized(qa, sa, q, scales, out_dtype=torch.float32, out=None, acc=None, stream=None):
+def tp_qgemm_w8a8_prequantized(qa, sa, q, scales, out_dtype=torch.float32, out=None, acc=None, workspace=None,
+                               stream=None):
     """C = (float(qa . q^T) * sa[m]) * s[n] on activation codes already made by
     tp_quantize_rows_int8; optionally also writes the int32 accumulators."""
     ldqa = _mat(qa, "qa")
@@ -192,7 +194,8 @@ def tp_qgemm_w8a8_prequantized(qa, sa, q, scales, out_dtype=torch.float32, out=N
         out = torch.empty((m, n), dtype=out_dtype, device=qa.device)
     ldc = _mat(out, "out")
     ld_acc = _mat(acc, "acc") if acc is not None else 0
+    ws, ws_bytes = _workspace(_lib.TP_OP_QGEMM_W8A8_PREQUANTIZED, m, n, k, TP_A_PREROTATED, qa.device, workspace)
     _lib.check(_lib.load().tp_qgemm_w8a8_prequantized(qa.data_ptr(), ldqa, sa.data_ptr(), q.data_ptr(), ldq,
                                                       scales.data_ptr(), m, n, k, out.data_ptr(), _dt(out), ldc,
-                                                      _ptr(acc), ld_acc, _stream(stream)))
+                                                      _ptr(acc), ld_acc, _ptr(ws), ws_bytes, _stream(stream)))
     return out

@@ -117,26 +117,62 @@ tp_status check_sizes(int64_t m, int64_t n, int64_t k) {
 
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-// Workspace layout: W8/W4 with TP_A_ROTATE: bf16 A' [m, k].
-// W8A8: int8 qa [m, k] then (256-byte aligned) fp32 sa [m].
-bool workspace_bytes_for(tp_op op, int64_t m, int64_t k, int a_flags, int64_t* out) {
+// Workspace layout. Front part: W8/W4 with TP_A_ROTATE, bf16 A' [m, k];
+// W8A8 (unless the caller takes the codes), int8 qa [m, k] then (256-byte
+// aligned) fp32 sa [m]. Then, 256-byte aligned, the split-K partial sums of
+// the small-M products (qgemm_partial_bytes; absent for larger M).
+struct WsLayout {
+  int64_t front = 0;     // bytes of the front part
+  int64_t part_off = 0;  // offset of the partial sums
+  int64_t total = 0;     // bytes needed
+};
+
+bool workspace_layout(tp_op op, int64_t m, int64_t n, int64_t k, int a_flags, bool own_codes, WsLayout* out) {
   int64_t mk;
   if (!mul_ok(m, k, &mk)) return false;
-  if (op == TP_OP_QGEMM_W8 || op == TP_OP_QGEMM_W4) {
-    if (a_flags != TP_A_ROTATE) {
-      *out = 0;
-      return true;
+  int kind;
+  WsLayout l;
+  switch (op) {
+    case TP_OP_QGEMM_W8:
+    case TP_OP_QGEMM_W4:
+      kind = op == TP_OP_QGEMM_W8 ? tp::GEMM_W8 : tp::GEMM_W4;
+      if (a_flags == TP_A_ROTATE && !mul_ok(mk, 2, &l.front)) return false;
+      break;
+    case TP_OP_QGEMM_W8A8: {
+      kind = tp::GEMM_W8A8;
+      if (!own_codes) {
+        int64_t sa;
+        if (!mul_ok(m, 4, &sa)) return false;
+        if (mk > INT64_MAX - 512 - sa) return false;
+        l.front = round_up(mk, 256) + sa;
+      }
+      break;
     }
-    return mul_ok(mk, 2, out);
+    case TP_OP_QGEMM_W8A8_PREQUANTIZED:
+      kind = tp::GEMM_W8A8;
+      break;
+    default:
+      return false;
   }
-  if (op == TP_OP_QGEMM_W8A8) {
-    int64_t sa;
-    if (!mul_ok(m, 4, &sa)) return false;
-    if (mk > INT64_MAX - 512 - sa) return false;
-    *out = round_up(mk, 256) + sa;
-    return true;
-  }
-  return false;
+  const int64_t part = tp::qgemm_partial_bytes(kind, m, n, k);
+  if (part < 0 || l.front > INT64_MAX - 512 - part) return false;
+  l.part_off = part > 0 ? round_up(l.front, 256) : l.front;
+  l.total = l.part_off + part;
+  *out = l;
+  return true;
+}
+
+// Checks the caller's workspace against the layout; stores its extent.
+tp_status check_workspace(const WsLayout& l, const void* ws, size_t ws_bytes, Extent* ew) {
+  *ew = Extent{};
+  if (l.total == 0) return TP_OK;
+  if (!ws || (uint64_t)ws_bytes < (uint64_t)l.total)
+    return fail(TP_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes given, %lld needed", ws_bytes,
+                (long long)l.total);
+  if (((uintptr_t)ws & 15u) != 0) return fail(TP_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  ew->lo = (uintptr_t)ws;
+  ew->hi = ew->lo + (uintptr_t)l.total;
+  return TP_OK;
 }
 
 }  // namespace
@@ -167,11 +203,10 @@ const char* tp_last_error_message(void) { return g_msg; }
 int tp_abi_version(void) { return TP_ABI_VERSION; }
 
 size_t tp_workspace_size(tp_op op, int64_t m, int64_t n, int64_t k, int a_flags) {
-  (void)n;
-  if (m < 0 || k <= 0) return 0;
-  int64_t b;
-  if (!workspace_bytes_for(op, m, k, a_flags, &b)) return 0;
-  return (size_t)b;
+  if (m < 0 || n < 0 || k <= 0 || k % 256 != 0 || m > INT_MAX || n > INT_MAX || k > INT_MAX) return 0;
+  WsLayout l;
+  if (!workspace_layout(op, m, n, k, a_flags, false, &l)) return 0;
+  return (size_t)l.total;
 }
 
 tp_status tp_rotate_quantize_weights(const void* w, tp_dtype w_dtype, int64_t n, int64_t k, int64_t ldw, int bits,
@@ -245,15 +280,9 @@ tp_status weight_only(int kind, const void* a, tp_dtype a_dtype, int64_t lda, in
   if (!mul_ok(n, kind == tp::GEMM_W8 ? 1 : k / 256, &ns)) return fail(TP_ERR_SIZE_OVERFLOW, "scale count overflows");
   TP_TRY(check_vector("w_scales", w_scales, ns, &es));
   TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec, dtype_size(c_dtype)));
-  int64_t need;
-  if (!workspace_bytes_for(op, m, k, a_flags, &need)) return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
-  if (need > 0) {
-    if (!ws || (int64_t)ws_bytes < need)
-      return fail(TP_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes given, %lld needed", ws_bytes, (long long)need);
-    if (((uintptr_t)ws & 15u) != 0) return fail(TP_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-    ew.lo = (uintptr_t)ws;
-    ew.hi = ew.lo + (uintptr_t)need;
-  }
+  WsLayout wl;
+  if (!workspace_layout(op, m, n, k, a_flags, false, &wl)) return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
+  TP_TRY(check_workspace(wl, ws, ws_bytes, &ew));
   if (overlaps(ec, ea) || overlaps(ec, eq) || overlaps(ec, es) || overlaps(ec, ew) || overlaps(ew, ea) ||
       overlaps(ew, eq) || overlaps(ew, es))
     return fail(TP_ERR_BAD_ALIASING, "c and the workspace must not overlap any other operand");
@@ -282,6 +311,7 @@ tp_status weight_only(int kind, const void* a, tp_dtype a_dtype, int64_t lda, in
   g.ldc = ldc;
   g.acc_out = nullptr;
   g.ld_acc = 0;
+  g.part = wl.total > wl.part_off ? (uint8_t*)ws + wl.part_off : nullptr;
   return hip_status(tp::launch_qgemm(g, stream), "product launch");
 }
 
@@ -321,17 +351,10 @@ tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flag
   if (qa_out) TP_TRY(check_matrix("qa_out", qa_out, m, k, k, 1, &eqa));
   if (sa_out) TP_TRY(check_vector("sa_out", sa_out, m, &esa));
   if (acc_out) TP_TRY(check_matrix("acc_out", acc_out, m, n * 4, ld_acc, 4, &eacc, 4));
-  int64_t need = 0;
-  if (!own_codes) {
-    if (!workspace_bytes_for(TP_OP_QGEMM_W8A8, m, k, a_flags, &need))
-      return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
-    if (!workspace || (int64_t)workspace_bytes < need)
-      return fail(TP_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes given, %lld needed", workspace_bytes,
-                  (long long)need);
-    if (((uintptr_t)workspace & 15u) != 0) return fail(TP_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-    ew.lo = (uintptr_t)workspace;
-    ew.hi = ew.lo + (uintptr_t)need;
-  }
+  WsLayout wl;
+  if (!workspace_layout(TP_OP_QGEMM_W8A8, m, n, k, a_flags, own_codes, &wl))
+    return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
+  TP_TRY(check_workspace(wl, workspace, workspace_bytes, &ew));
   const Extent* outs[] = {&ec, &eqa, &esa, &eacc, &ew};
   const Extent* ins[] = {&ea, &eq, &es};
   for (const Extent* o : outs) {
@@ -363,13 +386,14 @@ tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flag
   g.ldc = ldc;
   g.acc_out = acc_out;
   g.ld_acc = ld_acc;
+  g.part = wl.total > wl.part_off ? (uint8_t*)workspace + wl.part_off : nullptr;
   return hip_status(tp::launch_qgemm(g, stream), "product launch");
 }
 
 tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float* sa, const int8_t* q, int64_t ldq,
                                      const float* w_scales, int64_t m, int64_t n, int64_t k, void* c,
                                      tp_dtype c_dtype, int64_t ldc, int32_t* acc_out, int64_t ld_acc,
-                                     hipStream_t stream) {
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(c_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "c_dtype %d is not TP_F32 or TP_BF16", (int)c_dtype);
   TP_TRY(check_sizes(m, n, k));
   if (k > INT32_MAX / (127 * 127))
@@ -382,10 +406,17 @@ tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float
   TP_TRY(check_vector("w_scales", w_scales, n, &es));
   TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec, dtype_size(c_dtype)));
   if (acc_out) TP_TRY(check_matrix("acc_out", acc_out, m, n * 4, ld_acc, 4, &eacc, 4));
+  WsLayout wl;
+  Extent ew;
+  if (!workspace_layout(TP_OP_QGEMM_W8A8_PREQUANTIZED, m, n, k, TP_A_PREROTATED, true, &wl))
+    return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
+  TP_TRY(check_workspace(wl, workspace, workspace_bytes, &ew));
   const Extent* ins[] = {&eqa, &esa, &eq, &es};
   for (const Extent* i : ins)
-    if (overlaps(ec, *i) || overlaps(eacc, *i)) return fail(TP_ERR_BAD_ALIASING, "an output overlaps an input");
-  if (overlaps(ec, eacc)) return fail(TP_ERR_BAD_ALIASING, "c and acc_out overlap");
+    if (overlaps(ec, *i) || overlaps(eacc, *i) || overlaps(ew, *i))
+      return fail(TP_ERR_BAD_ALIASING, "an output or the workspace overlaps an input");
+  if (overlaps(ec, eacc) || overlaps(ec, ew) || overlaps(eacc, ew))
+    return fail(TP_ERR_BAD_ALIASING, "c, acc_out and the workspace must not overlap");
   if (m == 0 || n == 0) return ok();
   tp::GemmArgs g{};
   g.kind = tp::GEMM_W8A8;
@@ -403,6 +434,7 @@ tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float
   g.ldc = ldc;
   g.acc_out = acc_out;
   g.ld_acc = ld_acc;
+  g.part = wl.total > 0 ? workspace : nullptr;
   return hip_status(tp::launch_qgemm(g, stream), "product launch");
 }
 

@@ -19,9 +19,14 @@ namespace tp {
 #define LGKMCNT0_ENCODE 0xC07F
 
 // Workgroup barrier without the memory fence of __syncthreads(): waves wait
-// for each other, and the compiler may not move memory operations across it,
-// but no outstanding-memory wait is implied (callers wait explicitly).
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+// for each other, no outstanding-memory wait is implied (callers wait
+// explicitly), and the instruction scheduler may move nothing across it (a
+// plain memory clobber would still let it sink matrix instructions past it).
+__device__ __forceinline__ void barrier_only() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;

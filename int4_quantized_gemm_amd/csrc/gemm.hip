@@ -23,6 +23,7 @@
 
 #include "device_common.hpp"
 #include "gemm_pp.hpp"
+#include "gemm_skinny.hpp"
 #include "kernels.hpp"
 
 namespace tp {
@@ -300,6 +301,12 @@ static int pick_cfg(int kind, int64_t m, int64_t n, int64_t k) {
 }
 
 void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn) {
+  SkPlan sp;
+  if (skinny_plan(kind, m, n, k, &sp)) {
+    *bm = 16 * sp.fm;
+    *bn = SK_BN;
+    return;
+  }
   switch (pick_cfg(kind, m, n, k)) {
     case CFG_PP_256x256: *bm = 256; *bn = 256; return;
     case CFG_PP_256x128: *bm = 256; *bn = 128; return;
@@ -307,8 +314,21 @@ void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn)
   }
 }
 
+int64_t qgemm_partial_bytes(int kind, int64_t m, int64_t n, int64_t k) {
+  SkPlan p;
+  if (!skinny_plan(kind, m, n, k, &p) || p.splits == 1) return 0;
+  const int64_t mn = m * n;  // m <= SK_MAX_M, n < 2^31
+  if (mn > INT64_MAX / 4 / p.splits) return -1;
+  return mn * 4 * p.splits;
+}
+
 template <int KIND>
 static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
+  SkPlan sp;
+  if (skinny_plan(KIND, g.m, g.n, g.k, &sp)) {
+    if (sp.splits > 1 && !g.part) return hipErrorInvalidValue;
+    return launch_skinny<KIND>(g, sp, stream);
+  }
   switch (pick_cfg(KIND, g.m, g.n, g.k)) {
     case CFG_PP_256x256:
       if constexpr (KIND == GEMM_W8A8) return launch_pp<KIND, 256, 256, 128, 64, 4>(g, stream);

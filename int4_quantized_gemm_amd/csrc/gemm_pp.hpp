@@ -239,15 +239,29 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, fa[0][i]),
                                                              __builtin_bit_cast(i32x4_t, fb[j]), acc[i][j], 0, 0, 0);
     } else {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        bf16x8_t b0, b1;
+      // W8: the widening of fragment j+1 is interleaved with the MFMAs of
+      // fragment j, so one wave's VALU work runs while its matrix
+      // instructions execute (measured 3% faster at 4096x12288x3072; the same
+      // interleave made the int4 kernel slower, which keeps the plain order).
+      auto widen = [&](int j, bf16x8_t& b0, bf16x8_t& b1) {
         if constexpr (KIND == GEMM_W4) {
           b0 = pp_widen_i4x8(fb[j].x);
           b1 = pp_widen_i4x8(fb[j].y);
         } else {
           b0 = pp_widen_i8x8(fb[j].x, fb[j].y);
           b1 = pp_widen_i8x8(fb[j].z, fb[j].w);
+        }
+      };
+      bf16x8_t nb0, nb1;
+      widen(0, nb0, nb1);
+      if constexpr (KIND == GEMM_W8) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        bf16x8_t b0 = nb0, b1 = nb1;
+        if constexpr (KIND == GEMM_W8) {
+          if (j + 1 < FN) widen(j + 1, nb0, nb1);
+        } else if (j > 0) {
+          widen(j, b0, b1);
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -257,6 +271,14 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
         for (int i = 0; i < FM; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[1][i]), b1, acc[i][j],
                                                                0, 0, 0);
+      }
+      if constexpr (KIND == GEMM_W8) {
+#pragma unroll
+        for (int t = 0; t < 2 * FM * FN; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // then up to two VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if constexpr (KIND == GEMM_W4) {

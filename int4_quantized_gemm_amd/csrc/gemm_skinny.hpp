@@ -1,0 +1,383 @@
+// Quantized products with few activation rows (small M).
+//
+// With M up to a few dozen rows the product is bound by reading the weight
+// codes once from HBM, so the codes skip LDS: every wave loads its 16-row
+// weight fragments straight into registers in MFMA operand order and keeps two
+// 256-groups of them in flight. The block's activation rows for its K range
+// are staged once in LDS (rows past M are zero). K is split across blocks so
+// that all CUs stream a share of the weights; each split writes its partial
+// sums (fp32, or int32 for W8A8) to the workspace, and k_qgemm_reduce adds the
+// splits in split order (a fixed order, so the bytes of C do not depend on
+// timing) and applies the epilogue of the method:
+//   W8    C = (bf16(A') . q^T) * s[n]
+//   W4    C = sum_g s[n,g] * (bf16(A'_g) . q_g^T), folded per 256-group
+//   W8A8  acc = qa . q^T (int32, exact); C = (float(acc) * sa[m]) * sw[n]
+// (tensai docs, "画像生成", section "幅とメモリ" for the weight formats,
+// section "GPU" for the per-token activation codes.)
+//
+// Lane l of a wave owns weight row 16j + l % 16 of fragment j and the 16
+// bytes at 64t + 16 (l / 16) of each 64-byte piece t of that row's 256-group.
+// The two MFMA operands only need to agree on which K index each lane holds,
+// so the K order inside a piece follows the load:
+//   W8A8 (i8 16x16x64):  piece t, lane group g: K 64t + 16g + [0, 16).
+//   W8 (bf16 16x16x32):  the 16 codes split in halves h, one MFMA each:
+//                        K 64t + 16g + 8h + [0, 8).
+//   W4 (bf16 16x16x32):  a piece holds nibbles K 128t + 32g + [0, 32); dword d
+//                        feeds one MFMA with K 128t + 32g + 8d + [0, 8).
+// The activation fragment of the same MFMA reads those K indices from LDS.
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "gemm_pp.hpp"
+#include "kernels.hpp"
+
+namespace tp {
+
+template <int KIND>
+struct SkTraits {
+  static constexpr int AB = KIND == GEMM_W8A8 ? 1 : 2;     // activation bytes per element
+  static constexpr int WBG = KIND == GEMM_W4 ? 128 : 256;  // code bytes per weight row per 256-group
+  static constexpr int LPG = WBG / 64;                     // 16-byte loads per lane per fragment per group
+};
+
+constexpr int SK_FNW = 2;               // 16-row weight fragments per wave
+constexpr int SK_BN = 4 * 16 * SK_FNW;  // weight rows per block (four waves)
+constexpr int SK_DG = 2;                // 256-groups of codes in flight per wave
+
+template <int KIND, int FM, bool OUT_BF16, bool ACC_OUT, bool PARTIAL>
+__global__ __launch_bounds__(256) void k_qgemm_skinny(const uint8_t* __restrict__ A, int64_t lda_bytes,
+                                                      const uint8_t* __restrict__ B, int64_t ldb,
+                                                      const float* __restrict__ sw, const float* __restrict__ sa,
+                                                      int M, int N, int K, void* __restrict__ C, int64_t ldc,
+                                                      int32_t* __restrict__ acc_out, int64_t ld_acc,
+                                                      void* __restrict__ part, int nb, int splits, int gps) {
+  using T = SkTraits<KIND>;
+  constexpr int MR = 16 * FM;
+  constexpr bool I8 = KIND == GEMM_W8A8;
+  using acc_t = typename std::conditional<I8, i32x4_t, f32x4_t>::type;
+  extern __shared__ __align__(16) uint8_t sk_lds[];
+
+  const int pid = blockIdx.x;
+  const int nbi = pid % nb;
+  const int rest = pid / nb;
+  const int ks = rest % splits;
+  const int mbi = rest / splits;
+  const int G = K >> 8;
+  const int g0 = ks * gps;
+  const int ng = min(gps, G - g0);
+  const int m0 = mbi * MR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int nw0 = nbi * SK_BN + wave * 16 * SK_FNW;
+
+  const uint8_t* wrow[SK_FNW];
+  int ncol[SK_FNW];
+#pragma unroll
+  for (int j = 0; j < SK_FNW; ++j) {
+    ncol[j] = nw0 + 16 * j + r16;
+    const int n = min(ncol[j], N - 1);
+    wrow[j] = B + (int64_t)n * ldb + (int64_t)g0 * T::WBG + 16 * g4;
+  }
+
+  u32x4_t wr[SK_DG][SK_FNW][T::LPG];
+  auto load_group = [&](u32x4_t (&dst)[SK_FNW][T::LPG], int gi) {
+#pragma unroll
+    for (int j = 0; j < SK_FNW; ++j)
+#pragma unroll
+      for (int t = 0; t < T::LPG; ++t)
+        dst[j][t] = *reinterpret_cast<const u32x4_t*>(wrow[j] + (int64_t)gi * T::WBG + 64 * t);
+  };
+#pragma unroll
+  for (int d = 0; d < SK_DG; ++d)
+    if (d < ng) load_group(wr[d], d);
+
+  // Activation rows m0 .. m0+MR-1 (clamped to M-1: rows past M only feed
+  // output rows that are never stored), K range of this split, into LDS with
+  // direct-to-LDS loads. LDS slot (row r, 16-byte column c) sits at
+  // r * cpr + (c ^ (r & 15)), so the 16 rows of a fragment read fall in 16
+  // distinct bank groups. Each wave instruction fills 64 consecutive slots.
+  const int cpr = ng * 256 * T::AB / 16;  // 16-byte columns per row, a multiple of 16
+  {
+    const int total = MR * cpr;  // a multiple of 256
+    const uint8_t* abase = A + (int64_t)g0 * 256 * T::AB;
+    const int s = wave * 64 + lane;
+    int r = s / cpr, p = s - r * cpr;
+    for (int s0 = wave * 64; s0 < total; s0 += 256) {
+      const int c = p ^ (r & 15);
+      const int m = min(m0 + r, M - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(abase + (int64_t)m * lda_bytes + c * 16),
+                                       (lds_void_t*)(sk_lds + s0 * 16), 16, 0, 0);
+      p += 256;
+      while (p >= cpr) {
+        p -= cpr;
+        ++r;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(0));
+  __syncthreads();
+
+  acc_t acc[FM][SK_FNW];
+  f32x4_t tot[KIND == GEMM_W4 ? FM : 1][SK_FNW];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < SK_FNW; ++j) {
+      acc[i][j] = acc_t{};
+      if constexpr (KIND == GEMM_W4) tot[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // Fragment rows 16i + r16: all of a lane's reads share r16 & 15 = r16.
+  const int rowbytes = cpr * 16;
+  const uint8_t* arow = sk_lds + r16 * rowbytes;
+  auto afrag = [&](int i, int elem) -> u32x4_t {
+    const int c = (elem * T::AB) >> 4;
+    return *reinterpret_cast<const u32x4_t*>(arow + i * 16 * rowbytes + ((c ^ r16) << 4));
+  };
+
+  auto compute_group = [&](const u32x4_t (&w)[SK_FNW][T::LPG], int gi) {
+    const int kl = gi * 256;
+    if constexpr (I8) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        u32x4_t a[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[i] = afrag(i, kl + 64 * t + 16 * g4);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < SK_FNW; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a[i]),
+                                                               __builtin_bit_cast(i32x4_t, w[j][t]), acc[i][j], 0, 0,
+                                                               0);
+      }
+    } else if constexpr (KIND == GEMM_W8) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8_t b[SK_FNW];
+#pragma unroll
+          for (int j = 0; j < SK_FNW; ++j) {
+            // Opaque copies: without them the compiler splits the in-flight
+            // code words into one register per byte.
+            uint32_t lo = h == 0 ? w[j][t].x : w[j][t].z, hi = h == 0 ? w[j][t].y : w[j][t].w;
+            asm volatile("" : "+v"(lo), "+v"(hi));
+            b[j] = pp_widen_i8x8(lo, hi);
+          }
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const u32x4_t a = afrag(i, kl + 64 * t + 16 * g4 + 8 * h);
+#pragma unroll
+            for (int j = 0; j < SK_FNW; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), b[j], acc[i][j],
+                                                                   0, 0, 0);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          bf16x8_t b[SK_FNW];
+#pragma unroll
+          for (int j = 0; j < SK_FNW; ++j) {
+            const uint32_t word = d == 0 ? w[j][t].x : d == 1 ? w[j][t].y : d == 2 ? w[j][t].z : w[j][t].w;
+            b[j] = pp_widen_i4x8(word);
+          }
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const u32x4_t a = afrag(i, kl + 128 * t + 32 * g4 + 8 * d);
+#pragma unroll
+            for (int j = 0; j < SK_FNW; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), b[j], acc[i][j],
+                                                                   0, 0, 0);
+          }
+        }
+    }
+  };
+
+  for (int gb = 0; gb < ng; gb += SK_DG) {
+#pragma unroll
+    for (int d = 0; d < SK_DG; ++d) {
+      const int gi = gb + d;
+      if (gi < ng) {
+        float sg[SK_FNW];
+        if constexpr (KIND == GEMM_W4) {
+#pragma unroll
+          for (int j = 0; j < SK_FNW; ++j) sg[j] = sw[(int64_t)min(ncol[j], N - 1) * G + g0 + gi];
+        }
+        compute_group(wr[d], gi);
+        if (gi + SK_DG < ng) load_group(wr[d], gi + SK_DG);
+        if constexpr (KIND == GEMM_W4) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < SK_FNW; ++j) {
+              tot[i][j] += sg[j] * acc[i][j];
+              acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+      }
+    }
+  }
+
+  // Output: lane holds column ncol[j] and rows m0 + 16i + 4 g4 + r.
+#pragma unroll
+  for (int j = 0; j < SK_FNW; ++j) {
+    const int n = ncol[j];
+    if (n >= N) continue;
+    float scol = 1.f;
+    if constexpr (!PARTIAL && KIND != GEMM_W4) scol = sw[n];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * i + 4 * g4 + r;
+        if (m >= M) continue;
+        if constexpr (PARTIAL) {
+          const int64_t off = ((int64_t)ks * M + m) * N + n;
+          if constexpr (I8)
+            reinterpret_cast<int32_t*>(part)[off] = acc[i][j][r];
+          else if constexpr (KIND == GEMM_W4)
+            reinterpret_cast<float*>(part)[off] = tot[i][j][r];
+          else
+            reinterpret_cast<float*>(part)[off] = acc[i][j][r];
+        } else {
+          float y;
+          if constexpr (I8) {
+            if constexpr (ACC_OUT) acc_out[(int64_t)m * ld_acc + n] = acc[i][j][r];
+            y = ((float)acc[i][j][r] * sa[m]) * scol;
+          } else if constexpr (KIND == GEMM_W4) {
+            y = tot[i][j][r];
+          } else {
+            y = acc[i][j][r] * scol;
+          }
+          if constexpr (OUT_BF16)
+            reinterpret_cast<__bf16*>(C)[(int64_t)m * ldc + n] = (__bf16)y;
+          else
+            reinterpret_cast<float*>(C)[(int64_t)m * ldc + n] = y;
+        }
+      }
+  }
+}
+
+// Sum of the split partials in split order, then the epilogue. One thread per
+// output element; blockIdx.y is the row.
+template <int KIND, bool OUT_BF16, bool ACC_OUT>
+__global__ __launch_bounds__(256) void k_qgemm_reduce(const void* __restrict__ part, int splits, int M, int N,
+                                                      const float* __restrict__ sw, const float* __restrict__ sa,
+                                                      void* __restrict__ C, int64_t ldc,
+                                                      int32_t* __restrict__ acc_out, int64_t ld_acc) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int m = blockIdx.y;
+  if (n >= N) return;
+  const int64_t plane = (int64_t)M * N;
+  const int64_t off = (int64_t)m * N + n;
+  float y;
+  if constexpr (KIND == GEMM_W8A8) {
+    const int32_t* p = reinterpret_cast<const int32_t*>(part);
+    int32_t s = p[off];
+    for (int sp = 1; sp < splits; ++sp) s += p[sp * plane + off];
+    if constexpr (ACC_OUT) acc_out[(int64_t)m * ld_acc + n] = s;
+    y = ((float)s * sa[m]) * sw[n];
+  } else {
+    const float* p = reinterpret_cast<const float*>(part);
+    float s = p[off];
+    for (int sp = 1; sp < splits; ++sp) s += p[sp * plane + off];
+    y = KIND == GEMM_W8 ? s * sw[n] : s;
+  }
+  if constexpr (OUT_BF16)
+    reinterpret_cast<__bf16*>(C)[(int64_t)m * ldc + n] = (__bf16)y;
+  else
+    reinterpret_cast<float*>(C)[(int64_t)m * ldc + n] = y;
+}
+
+// Launch plan of the small-M path for one product shape.
+struct SkPlan {
+  int fm;      // 16-row activation fragments per block (1, 2 or 4)
+  int mb;      // blocks along M
+  int nb;      // blocks along N
+  int splits;  // blocks along K
+  int gps;     // 256-groups per split (the last split may hold fewer)
+  int lds;     // dynamic LDS bytes per block
+};
+
+constexpr int SK_MAX_M = 64;           // rows up to which the small-M path is used
+constexpr int SK_TARGET_BLOCKS = 512;  // two blocks per CU
+constexpr int SK_MAX_LDS = 64 * 1024;  // activation stage per block (the default dynamic-LDS limit)
+
+inline bool skinny_plan(int kind, int64_t m, int64_t n, int64_t k, SkPlan* p) {
+  if (m < 1 || m > SK_MAX_M || n < 1 || k < 256) return false;
+  const int fm = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+  const int mr = 16 * fm;
+  const int ab = kind == GEMM_W8A8 ? 1 : 2;
+  const int64_t G = k / 256;
+  const int64_t mb = (m + mr - 1) / mr;
+  const int64_t nb = (n + SK_BN - 1) / SK_BN;
+  const int64_t gmax = SK_MAX_LDS / mr / (256 * ab);
+  const int64_t base = nb * mb;
+  if (gmax < 1 || base > INT32_MAX) return false;
+  int64_t splits = (SK_TARGET_BLOCKS + base - 1) / base;
+  if (splits > G) splits = G;
+  if (splits < 1) splits = 1;
+  int64_t gps = (G + splits - 1) / splits;
+  if (gps > gmax) gps = gmax;
+  splits = (G + gps - 1) / gps;
+  if (base * splits > INT32_MAX) return false;
+  p->fm = fm;
+  p->mb = (int)mb;
+  p->nb = (int)nb;
+  p->splits = (int)splits;
+  p->gps = (int)gps;
+  p->lds = mr * (int)(gps * 256 * ab);
+  return true;
+}
+
+template <int KIND, int FM>
+static hipError_t launch_skinny_fm(const GemmArgs& g, const SkPlan& p, hipStream_t stream) {
+  const int64_t lda_bytes = g.lda * (KIND == GEMM_W8A8 ? 1 : 2);
+  const uint8_t* a = (const uint8_t*)g.a;
+  const uint8_t* b = (const uint8_t*)g.b;
+  const dim3 grid((unsigned)(p.nb * p.splits * p.mb)), block(256);
+  const bool split = p.splits > 1;
+#define TP_LAUNCH_SK(OB, AO, PA)                                                                                 \
+  hipLaunchKernelGGL((k_qgemm_skinny<KIND, FM, OB, AO, PA>), grid, block, p.lds, stream, a, lda_bytes, b, g.ldb, \
+                     g.w_scales, g.a_scales, (int)g.m, (int)g.n, (int)g.k, g.c, g.ldc, g.acc_out, g.ld_acc, g.part, \
+                     p.nb, p.splits, p.gps)
+  if (split) {
+    TP_LAUNCH_SK(false, false, true);
+  } else if (KIND == GEMM_W8A8 && g.acc_out) {
+    if (g.c_bf16) TP_LAUNCH_SK(true, true, false); else TP_LAUNCH_SK(false, true, false);
+  } else {
+    if (g.c_bf16) TP_LAUNCH_SK(true, false, false); else TP_LAUNCH_SK(false, false, false);
+  }
+#undef TP_LAUNCH_SK
+  if (!split) return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 rgrid((unsigned)((g.n + 255) / 256), (unsigned)g.m), rblock(256);
+#define TP_LAUNCH_RED(OB, AO)                                                                                     \
+  hipLaunchKernelGGL((k_qgemm_reduce<KIND, OB, AO>), rgrid, rblock, 0, stream, g.part, p.splits, (int)g.m,        \
+                     (int)g.n, g.w_scales, g.a_scales, g.c, g.ldc, g.acc_out, g.ld_acc)
+  if (KIND == GEMM_W8A8 && g.acc_out) {
+    if (g.c_bf16) TP_LAUNCH_RED(true, true); else TP_LAUNCH_RED(false, true);
+  } else {
+    if (g.c_bf16) TP_LAUNCH_RED(true, false); else TP_LAUNCH_RED(false, false);
+  }
+#undef TP_LAUNCH_RED
+  return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t launch_skinny(const GemmArgs& g, const SkPlan& p, hipStream_t stream) {
+  switch (p.fm) {
+    case 1: return launch_skinny_fm<KIND, 1>(g, p, stream);
+    case 2: return launch_skinny_fm<KIND, 2>(g, p, stream);
+    default: return launch_skinny_fm<KIND, 4>(g, p, stream);
+  }
+}
+
+}  // namespace tp

@@ -32,11 +32,16 @@ struct GemmArgs {
   int64_t ldc;              // elements
   int32_t* acc_out;         // optional int32 [m, n] (W8A8)
   int64_t ld_acc;
+  void* part;               // split-K partial sums, qgemm_partial_bytes() bytes (may be null when that is 0)
 };
 
 hipError_t launch_qgemm(const GemmArgs& args, hipStream_t stream);
 
 // Tile configuration chosen for a shape (exposed for the benchmark's reports).
 void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn);
+
+// Bytes of split-K partial sums launch_qgemm needs for this shape (0 when the
+// product runs unsplit); -1 when the size overflows.
+int64_t qgemm_partial_bytes(int kind, int64_t m, int64_t n, int64_t k);
 
 }  // namespace tp

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.tp_abi_version() == 1
+    assert lib.tp_abi_version() == 2
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.tp_status_string(code).decode() == name
 
@@ -125,7 +125,9 @@ def test_quantize_rows_refusals(lib, kw, status):
 
 # ------------------------------------------------------------ products
 def w8(lib, fn="tp_qgemm_w8", a=A, ad=1, lda=512, flags=1, q=B, ldq=512, s=C, m=64, n=256, k=512, c=D, cd=1,
-       ldc=256, ws=E, wsb=64 * 512 * 2):
+       ldc=256, ws=E, wsb=None):
+    if wsb is None:  # what the library asks for (rotated A' and split-K partial sums)
+        wsb = lib.tp_workspace_size(1 if fn == "tp_qgemm_w8" else 2, 64, 256, 512, 1)
     return getattr(lib, fn)(a, ad, lda, flags, q, ldq, s, m, n, k, c, cd, ldc, ws, wsb, None)
 
 
@@ -173,7 +175,8 @@ def w8a8(lib, a=A, ad=1, lda=512, flags=1, q=B, ldq=512, s=C, m=64, n=256, k=512
     (dict(acc=D, ld_acc=256), 10),                   # acc_out overlaps c
     (dict(c=B), 10),                                 # c overlaps q
     (dict(flags=-1), 11),
-    (dict(qa=0x30000000, sa=0x30000000 + 64 * 512 - 4, ws=0, wsb=0), 10),
+    (dict(qa=0x30000000, sa=0x30000000 + 64 * 512 - 4), 10),
+    (dict(m=16, qa=0x30000000, sa=0x38000000, ws=0, wsb=0), 9),   # split-K partial sums still need room
 ])
 def test_w8a8_refusals(lib, kw, status):
     assert w8a8(lib, **kw) == status, _err(lib)
@@ -183,6 +186,39 @@ def test_w8a8_own_codes_need_no_workspace(lib):
     assert w8a8(lib, m=0, qa=0x30000000, sa=0x38000000, ws=0, wsb=0) == 0
 
 
+def test_small_m_workspace_refusals(lib):
+    # a pre-rotated small-M product still needs room for its partial sums
+    assert w8(lib, flags=0, m=16, ws=0, wsb=0) == 9
+    need = lib.tp_workspace_size(1, 16, 256, 512, 0)
+    assert need > 0
+    assert w8(lib, flags=0, m=16, wsb=need - 1) == 9
+    assert w8(lib, flags=0, m=16, ws=E + 8, wsb=need) == 5
+
+
+def pq(lib, qa=A, ldqa=512, sa=C, q=B, ldq=512, s=C + 4096, m=64, n=256, k=512, c=D, cd=0, ldc=256, acc=0, ld_acc=0,
+       ws=E, wsb=1 << 20):
+    return lib.tp_qgemm_w8a8_prequantized(qa, ldqa, sa, q, ldq, s, m, n, k, c, cd, ldc, acc or None, ld_acc,
+                                          ws or None, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=0, wsb=0), 9),            # m <= 64: split-K partial sums need a workspace
+    (dict(wsb=1000), 9),
+    (dict(ws=E + 4), 5),
+    (dict(ws=A), 10),                  # workspace overlaps qa
+    (dict(ws=D), 10),                  # workspace overlaps c
+    (dict(k=300, ldqa=512, ldq=512), 3),
+    (dict(cd=3), 6),
+])
+def test_prequantized_refusals(lib, kw, status):
+    assert pq(lib, **kw) == status, _err(lib)
+
+
+def test_prequantized_large_m_needs_no_workspace(lib):
+    assert lib.tp_workspace_size(4, 4096, 9216, 3072, 0) == 0
+    assert pq(lib, m=0, ws=0, wsb=0) == 0
+
+
 def test_workspace_sizes(lib):
     assert lib.tp_workspace_size(1, 4096, 12288, 3072, 1) == 4096 * 3072 * 2
     assert lib.tp_workspace_size(2, 4032, 3072, 12288, 1) == 4032 * 12288 * 2
@@ -190,6 +226,26 @@ def test_workspace_sizes(lib):
     assert lib.tp_workspace_size(3, 4096, 9216, 3072, 1) == 4096 * 3072 + 4096 * 4
     assert lib.tp_workspace_size(3, 3, 9216, 256, 1) == 768 + 12
     assert lib.tp_workspace_size(3, -1, 9, 256, 1) == 0
+    assert lib.tp_workspace_size(4, 4096, 9216, 3072, 0) == 0
+
+
+def test_workspace_sizes_small_m(lib):
+    # Few rows: split-K partial sums (4 m n bytes per split) follow the front
+    # part, 256-byte aligned; the split count does not depend on a_flags.
+    m, n, k = 64, 12288, 3072
+    pre = lib.tp_workspace_size(1, m, n, k, 0)
+    rot = lib.tp_workspace_size(1, m, n, k, 1)
+    assert pre > 0 and pre % (4 * m * n) == 0
+    assert rot == (m * k * 2 + 255) // 256 * 256 + pre
+    w8a8_pre = lib.tp_workspace_size(4, m, n, k, 0)
+    assert w8a8_pre > 0 and w8a8_pre % (4 * m * n) == 0
+    front = (m * k + 255) // 256 * 256 + 4 * m
+    assert lib.tp_workspace_size(3, m, n, k, 1) == (front + 255) // 256 * 256 + w8a8_pre
+    # one 256-group cannot be split
+    assert lib.tp_workspace_size(1, 1, 256, 256, 0) == 0
+    # above the small-M range nothing but the front part
+    assert lib.tp_workspace_size(1, 65, n, k, 0) == 0
+    assert lib.tp_workspace_size(1, 3, 9, 255, 0) == 0
 
 
 def test_binding_refuses_cpu_tensors():

@@ -317,6 +317,83 @@ def test_w8a8_ragged(m, n, k):
     _w8a8_case(W.TINY.with_(m=m, n=n, k=k, seed=m + 3 * n, act_outliers=2, w_outliers=2, path="w8a8"))
 
 
+# ------------------------------------------------------------ few rows (M <= 64)
+def _small_m_case(kind, wl, rows=None, out_dtype=torch.float32):
+    """One small-M product against the oracle; returns the device output."""
+    d = dev()
+    x, w = W.generate(wl, rows=rows)
+    bits = 4 if kind == "w4" else 8
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=bits)
+    rq, rs = oracle_weights(wl, w, bits)
+    if kind == "w8a8":
+        y, qa, sa, acc = tp.tp_qgemm_w8a8(x.to(d), q, s, rotate=True, out_dtype=out_dtype, want_codes=True,
+                                          want_acc=True)
+        ry, racc, rqa, rsa = oracle.qgemm_w8a8(f64(x), rq, rs)
+        assert np.array_equal(host(sa), rsa), "activation scales differ"
+        assert np.array_equal(host(qa), rqa), "activation codes differ"
+        gacc = host(acc).astype(np.int64)
+        assert np.array_equal(gacc, racc), f"{int(np.sum(gacc != racc))} int32 accumulators differ"
+        if out_dtype == torch.float32:
+            assert_w8a8_out(f64(y), ry, f"w8a8 small-m {wl.name}")
+        # the same codes through the prequantized entry point: the same bytes
+        y2 = tp.tp_qgemm_w8a8_prequantized(qa, sa, q, s, out_dtype=out_dtype)
+        assert torch.equal(y, y2)
+    else:
+        fn = tp.tp_qgemm_w8 if kind == "w8" else tp.tp_qgemm_w4
+        y = fn(x.to(d), q, s, rotate=True, out_dtype=out_dtype)
+        ref = (oracle.qgemm_w8 if kind == "w8" else oracle.qgemm_w4)(f64(x), rq, rs)
+        err = assert_bf16_path(f64(y), ref, f"{kind} small-m {wl.name}")
+        if out_dtype == torch.float32:
+            assert err < 1e-4
+        y2 = fn(x.to(d), q, s, rotate=True, out_dtype=out_dtype)
+        assert torch.equal(y, y2), "split-K result is not reproducible"
+    return y
+
+
+@pytest.mark.parametrize("kind", ["w8", "w4", "w8a8"])
+@pytest.mark.parametrize("m,n,k", [(1, 300, 512), (5, 1000, 2560), (16, 129, 256), (17, 777, 1536),
+                                   (33, 4000, 768), (64, 515, 3072), (64, 128, 12288)])
+def test_small_m_ragged(kind, m, n, k):
+    """Few-row products: split-K with several 256-groups per split, ragged N,
+    M not a multiple of 16, a single 256-group (no split)."""
+    announce("small-m", kind, m, n, k)
+    wl = W.TINY.with_(name=f"smallm_{m}_{n}_{k}", m=m, n=n, k=k, seed=m * 31 + n + k, act_outliers=2,
+                      w_outliers=2, path=kind)
+    _small_m_case(kind, wl)
+
+
+@pytest.mark.parametrize("name,kind", [("ffn_up", "w8"), ("ffn_down", "w4"), ("dit_qkv", "w8a8"),
+                                       ("dit_gateup", "w8a8")])
+@pytest.mark.parametrize("rows", [1, 16, 64])
+def test_small_m_full_weights(name, kind, rows):
+    """The first rows of the full-size workloads against their full weights
+    (the M <= 64 sweep the benchmark times), every output element."""
+    wl = W.BY_NAME[name]
+    announce("small-m full weights", name, kind, rows)
+    out = torch.bfloat16 if kind != "w8a8" else torch.float32
+    _small_m_case(kind, wl, rows=rows, out_dtype=out)
+
+
+def test_small_m_bf16_out_and_views():
+    """bf16 output of W8A8 and a padded output view on the split-K path."""
+    d = dev()
+    announce("small-m bf16 out / padded views")
+    wl = W.TINY.with_(name="smallm_views", m=20, n=700, k=2048, seed=77, path="w8a8")
+    x, w = W.generate(wl)
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    rq, rs = oracle_weights(wl, w, 8)
+    y32 = tp.tp_qgemm_w8a8(x.to(d), q, s, rotate=True)
+    ybf = tp.tp_qgemm_w8a8(x.to(d), q, s, rotate=True, out_dtype=torch.bfloat16)
+    assert torch.equal(ybf, y32.to(torch.bfloat16)), "bf16 output is not the RNE rounding of the fp32 one"
+    cbuf = torch.full((24, 700 + 40), 5.0, dtype=torch.float32, device=d)
+    out = cbuf[2:22, 8:708]
+    tp.tp_qgemm_w8(x.to(d), q, s, rotate=True, out=out)
+    ref = oracle.qgemm_w8(f64(x), rq, rs)
+    assert_bf16_path(f64(out), ref, "w8 small-m view")
+    assert torch.all(cbuf[:2] == 5.0) and torch.all(cbuf[22:] == 5.0)
+    assert torch.all(cbuf[:, :8] == 5.0) and torch.all(cbuf[:, 708:] == 5.0)
+
+
 @pytest.mark.parametrize("kind,m,n,k", [("w8a8", 4000, 9000, 768), ("w8", 4000, 8000, 512),
                                         ("w4", 4000, 8000, 1024), ("w8a8", 2100, 9000, 256)])
 def test_multistage_path_ragged(kind, m, n, k):
