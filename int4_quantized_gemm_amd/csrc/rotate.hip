@@ -13,6 +13,8 @@
 // Work layout: a 256-group is held by 32 lanes (a half wave), 8 consecutive
 // elements per lane, so every global access is a 16- or 32-byte vector per
 // lane and the transform needs 3 in-lane and 5 cross-lane butterfly stages.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -107,6 +109,350 @@ __global__ __launch_bounds__(256) void k_rotq_rows(const TIn* x, int64_t ldx, in
   }
 }
 
+// ------------------------------- rotate and quantize rows to int8 (fast path)
+// The same codes and scales as k_rotq_rows<MODE_I8_ROW>, computed in fp32 with
+// a proven error bound and redone exactly (fp64) only where the bound cannot
+// decide.
+//
+// Layout: a 256-group is held by one 16-lane row of the wave. Lane l loads
+// elements 16 l + i (i = 0..15, index bits 0-3 in registers) and applies the
+// four butterfly stages of those bits; the row then transposes the group
+// through LDS so that lane l holds elements l + 16 r (bits 4-7 in registers)
+// and applies the other four stages. Outputs stay in that order; the codes go
+// back through LDS to be stored 16 contiguous bytes per lane.
+//
+// Error bound (unnormalized transform, fp32 round-to-nearest): the rounding
+// errors that reach one output are those of the nodes of its butterfly tree;
+// at each of the 8 stages these nodes partition the 256 inputs, so each stage
+// adds at most 2^-24 * L1 (L1 = sum of |inputs| of the group) and the output
+// error is at most 8 * 2^-24 * L1 = 2^-21 L1 (before the exact 1/16).
+//   * Row maximum: elements whose fp32 magnitude is within twice the largest
+//     bound of the fp32 maximum are the only ones that can be the true
+//     maximum; their groups are transformed again in fp64 (exact for these
+//     inputs, as in k_rotq_rows) and the scale comes from the exact maximum.
+//   * Codes: t = v * (1/(16 s)) in fp32 is within B / (16 s) + 2^-22 (|t| + 1)
+//     of the exact quotient; a code whose t is at least that far from every
+//     half-integer rounds the same way as the exact one. A group with a code
+//     closer than that is redone in fp64 with quant_code (the reference rule).
+
+template <int M>
+__device__ __forceinline__ int dpp_xor(int v) {
+  if constexpr (M == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  if constexpr (M == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  if constexpr (M == 4)  // half mirror (i ^ 7), then quad reverse (i ^ 3)
+    return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF, false);
+  if constexpr (M == 8)  // mirror (i ^ 15), then half mirror (i ^ 7)
+    return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false), 0x141, 0xF, 0xF, false);
+  return v;
+}
+
+template <int M>
+__device__ __forceinline__ float xor16(float v) {
+  return __builtin_bit_cast(float, dpp_xor<M>(__builtin_bit_cast(int, v)));
+}
+
+// Sum over the 16 lanes of a row (every lane gets the total).
+__device__ __forceinline__ float sum16(float v) {
+  v += xor16<1>(v);
+  v += xor16<2>(v);
+  v += xor16<4>(v);
+  v += xor16<8>(v);
+  return v;
+}
+
+// Bitwise or over the 16 lanes of a row (every lane gets the result).
+__device__ __forceinline__ uint32_t or16(uint32_t v) {
+  v |= (uint32_t)dpp_xor<1>((int)v);
+  v |= (uint32_t)dpp_xor<2>((int)v);
+  v |= (uint32_t)dpp_xor<4>((int)v);
+  v |= (uint32_t)dpp_xor<8>((int)v);
+  return v;
+}
+
+// Four butterfly stages over the register index of 16 values.
+template <typename T>
+__device__ __forceinline__ void fwht16_regs(T (&v)[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i & h) == 0) {
+        const T a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+}
+
+// Orders this wave's LDS writes before its later LDS reads (one wave: the LDS
+// unit runs its operations in order; this keeps the compiler from reordering).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Row transpose: lane l gives elements 16 l + i, receives elements l + 16 r.
+// buf: this row's LDS area, touched by its 16 lanes only. Element e sits at
+// e + PAD * (e / 16) so that neither side of the exchange has bank conflicts.
+template <typename T>
+__device__ __forceinline__ void transpose16(T (&v)[16], T* buf, int l16) {
+  constexpr int PAD = sizeof(T) == 4 ? 4 : 2;
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) buf[(16 + PAD) * l16 + i] = v[i];
+  wave_lds_sync();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = buf[l16 + (16 + PAD) * r];
+}
+
+// The 16 inputs of one lane for one group, kept as loaded (bf16 pairs or fp32)
+// for the exact fallbacks.
+template <typename TIn>
+struct Raw16;
+
+template <>
+struct Raw16<uint16_t> {
+  uint32_t w[8];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    const uint4 a = reinterpret_cast<const uint4*>(p)[0], b = reinterpret_cast<const uint4*>(p)[1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = 0u;
+  }
+  __device__ __forceinline__ float get(int i) const { return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]); }
+};
+
+template <>
+struct Raw16<float> {
+  float w[16];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 f = reinterpret_cast<const float4*>(p)[c];
+      w[4 * c] = f.x; w[4 * c + 1] = f.y; w[4 * c + 2] = f.z; w[4 * c + 3] = f.w;
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = 0.f;
+  }
+  __device__ __forceinline__ float get(int i) const { return w[i]; }
+};
+
+template <int M>
+__device__ __forceinline__ double xor16d(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)dpp_xor<M>((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)dpp_xor<M>((int)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Exact (fp64) unnormalized rotated element e of a group, summed over the 16
+// lanes of the row (lane l holds inputs 16 l .. 16 l + 15 in raw): the sign of
+// input i is (-1)^popcount(i & e). Without rotation, input e itself. Every
+// lane of the row must be active; all get the value.
+template <typename TIn>
+__device__ __forceinline__ double exact_elem(const Raw16<TIn>& raw, bool rotate, int e, int l16) {
+  double acc = 0.0;
+  if (rotate) {
+    const int lpar = __builtin_popcount((unsigned)(l16 & (e >> 4))) & 1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int par = lpar ^ (__builtin_popcount((unsigned)(i & e)) & 1);
+      const double xi = (double)raw.get(i);
+      acc += par ? -xi : xi;
+    }
+  } else {
+    // input e lives in lane e / 16, register e % 16
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i == (e & 15)) acc = (double)raw.get(i);
+    acc = (l16 == (e >> 4)) ? acc : 0.0;
+  }
+  acc += xor16d<1>(acc);
+  acc += xor16d<2>(acc);
+  acc += xor16d<4>(acc);
+  acc += xor16d<8>(acc);
+  return acc;
+}
+
+constexpr int RQ_ROW_BYTES = 1280 + 64;  // LDS per 16-lane row: 256 padded floats
+constexpr float RQ_MAGIC = 12582912.0f;  // 1.5 * 2^23: adding it rounds to an integer (RNE)
+
+// WPR = 1: one wave per row, four rows per block (k <= 12 * 256).
+// WPR = 4: one block per row, the four waves split the groups (k <= 48 * 256).
+// Three waves per SIMD: the register budget (166) that keeps every input in
+// registers for the exact fallbacks without spilling.
+template <typename TIn, int WPR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_rotq_i8_fast(const TIn* __restrict__ x, int64_t ldx, int64_t rows,
+                                                      int groups, int rotate, int8_t* __restrict__ q, int64_t ldq,
+                                                      float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int set = lane >> 4, l16 = lane & 15;
+  __shared__ __align__(16) uint8_t lds[16 * RQ_ROW_BYTES];
+  __shared__ float red[2][4];
+  __shared__ double red64[4];
+  uint8_t* mybuf = lds + (wave * 4 + set) * RQ_ROW_BYTES;
+  float* fbuf = reinterpret_cast<float*>(mybuf);
+  int64_t row;
+  int gb, ge;
+  if constexpr (WPR == 1) {
+    row = (int64_t)blockIdx.x * 4 + wave;
+    if (row >= rows) return;  // uniform over the wave; no block barrier below
+    gb = 0;
+    ge = groups;
+  } else {
+    row = blockIdx.x;
+    const int gpw = (groups + 3) / 4;
+    gb = min(groups, wave * gpw);
+    ge = min(groups, gb + gpw);
+  }
+  const TIn* xr = x + row * ldx;
+
+  // Load every group of this wave (up to 3 per 16-lane row) and transform it.
+  Raw16<TIn> raw[3];
+  float v[3][16];
+  float bnd[3];
+  bool has[3];
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    has[u] = gb + set + 4 * u < ge;
+    if (has[u])
+      raw[u].load(xr + (int64_t)(gb + set + 4 * u) * 256 + l16 * 16);
+    else
+      raw[u].zero();
+  }
+  float amax = 0.f, bmax = 0.f;
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[u][i] = raw[u].get(i);
+    bnd[u] = 0.f;
+    if (rotate) {
+      float l1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) l1 += fabsf(v[u][i]);
+      l1 = sum16(l1);  // rows without a group hold zeros
+      fwht16_regs(v[u]);
+      transpose16(v[u], fbuf, l16);
+      fwht16_regs(v[u]);
+      bnd[u] = l1 * 0x1.00004p-21f;  // 2^-21 L1, rounded up
+    } else {
+      transpose16(v[u], fbuf, l16);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
+    bmax = fmaxf(bmax, bnd[u]);
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+  if constexpr (WPR == 4) {
+    if (lane == 0) {
+      red[0][wave] = amax;
+      red[1][wave] = bmax;
+    }
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    bmax = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  }
+
+  // Exact row maximum (unnormalized): the exact value of every element that
+  // could be the maximum. Candidates are kept as per-lane register bitmasks,
+  // so the loops below index no register array.
+  double amax_ex = (double)amax;
+  if (bmax > 0.f) {
+    const float thr = amax - 2.f * bmax;
+    double m_ex = 0.0;
+    auto scan = [&](auto uc) {
+      constexpr int U = decltype(uc)::value;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bits |= (uint32_t)(has[U] && fabsf(v[U][r]) >= thr) << r;
+      uint32_t rmask = or16(bits);  // registers that hold a candidate in some lane of this row
+      while (rmask) {               // uniform over this 16-lane row
+        const int r = __builtin_ctz(rmask);
+        rmask &= rmask - 1;
+        uint32_t lmask = (uint32_t)(__ballot((bits >> r) & 1u) >> (16 * set)) & 0xFFFFu;
+        while (lmask) {
+          const int lc = __builtin_ctz(lmask);
+          lmask &= lmask - 1;
+          m_ex = fmax(m_ex, fabs(exact_elem(raw[U], true, lc + 16 * r, l16)));
+        }
+      }
+    };
+    scan(std::integral_constant<int, 0>{});
+    scan(std::integral_constant<int, 1>{});
+    scan(std::integral_constant<int, 2>{});
+    m_ex = wave_max(m_ex);
+    if constexpr (WPR == 4) {
+      if (lane == 0) red64[wave] = m_ex;
+      __syncthreads();
+      m_ex = fmax(fmax(red64[0], red64[1]), fmax(red64[2], red64[3]));
+    }
+    amax_ex = m_ex;
+  }
+  const double unscale = rotate ? 0.0625 : 1.0;  // outputs above are 16 x the rotation (exact)
+  const float s = (float)(amax_ex * unscale / 127.0);
+  const double s64 = (double)s;
+  const double inv64 = s > 0.0f ? 1.0 / s64 : 0.0;
+  const float inv = (float)(inv64 * unscale);  // applied to the unnormalized outputs
+
+  // Codes, one group at a time. t = v * inv clamped to [-127, 127] (clamping
+  // first only removes cases that clamp either way); t + 1.5 * 2^23 rounds to
+  // the nearest integer, whose two's complement sits in the low byte. Codes
+  // the fp32 bound cannot decide get the exact value and the reference rule.
+  int8_t* qr = q + row * ldq;
+  auto codes = [&](auto uc) {
+    constexpr int U = decltype(uc)::value;
+    uint32_t code[16];
+    uint32_t bits = 0;
+    const float lim = 0.5f - (bnd[U] * inv * 1.0001f + 129.f * 0x1p-22f);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float t = __builtin_amdgcn_fmed3f(v[U][r] * inv, -127.f, 127.f);
+      const float f = t + RQ_MAGIC;
+      bits |= (uint32_t)(has[U] && fabsf(t - (f - RQ_MAGIC)) >= lim) << r;
+      code[r] = __builtin_bit_cast(uint32_t, f);
+    }
+    if (__ballot(bits != 0u)) {
+      uint32_t rmask = or16(bits);
+      while (rmask) {  // uniform over this 16-lane row
+        const int r = __builtin_ctz(rmask);
+        rmask &= rmask - 1;
+        uint32_t lmask = (uint32_t)(__ballot((bits >> r) & 1u) >> (16 * set)) & 0xFFFFu;
+        while (lmask) {
+          const int lc = __builtin_ctz(lmask);
+          lmask &= lmask - 1;
+          const double xe = exact_elem(raw[U], rotate != 0, lc + 16 * r, l16);
+          const uint32_t c = (uint32_t)quant_code(xe * unscale, s64, inv64, 127.0);
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) code[rr] = (rr == r && l16 == lc) ? c : code[rr];
+        }
+      }
+    }
+    // element l16 + 16 r -> byte l16 + 16 r of this row's buffer, then 16
+    // contiguous bytes per lane out
+    wave_lds_sync();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mybuf[l16 + 16 * r] = (uint8_t)code[r];
+    wave_lds_sync();
+    const uint4 w4 = *reinterpret_cast<const uint4*>(mybuf + 16 * l16);
+    if (has[U]) *reinterpret_cast<uint4*>(qr + (int64_t)(gb + set + 4 * U) * 256 + l16 * 16) = w4;
+  };
+  codes(std::integral_constant<int, 0>{});
+  codes(std::integral_constant<int, 1>{});
+  codes(std::integral_constant<int, 2>{});
+  if (lane == 0 && (WPR == 1 || wave == 0)) scales[row] = s;
+}
+
 // ------------------------------------------------------------------ launchers
 hipError_t launch_rotate_rows(const void* x, bool x_bf16, int64_t ldx, void* y, bool y_bf16, int64_t ldy,
                               int64_t m, int64_t k, hipStream_t stream) {
@@ -134,7 +480,25 @@ hipError_t launch_rotq_rows(const void* x, bool x_bf16, int64_t ldx, int64_t row
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   uint8_t* qb = (uint8_t*)q;
   const int rot = rotate ? 1 : 0;
-  if (bits == 8) {
+  if (bits == 8 && groups <= 48) {
+    int8_t* q8 = (int8_t*)q;
+    if (groups <= 12) {
+      if (x_bf16)
+        hipLaunchKernelGGL((k_rotq_i8_fast<uint16_t, 1>), grid, block, 0, stream, (const uint16_t*)x, ldx, rows,
+                           groups, rot, q8, ldq, scales);
+      else
+        hipLaunchKernelGGL((k_rotq_i8_fast<float, 1>), grid, block, 0, stream, (const float*)x, ldx, rows, groups,
+                           rot, q8, ldq, scales);
+    } else {
+      const dim3 grid_rows((unsigned)rows);
+      if (x_bf16)
+        hipLaunchKernelGGL((k_rotq_i8_fast<uint16_t, 4>), grid_rows, block, 0, stream, (const uint16_t*)x, ldx,
+                           rows, groups, rot, q8, ldq, scales);
+      else
+        hipLaunchKernelGGL((k_rotq_i8_fast<float, 4>), grid_rows, block, 0, stream, (const float*)x, ldx, rows,
+                           groups, rot, q8, ldq, scales);
+    }
+  } else if (bits == 8) {
     if (x_bf16)
       hipLaunchKernelGGL((k_rotq_rows<uint16_t, MODE_I8_ROW>), grid, block, 0, stream, (const uint16_t*)x, ldx,
                          rows, groups, rot, qb, ldq, scales);
