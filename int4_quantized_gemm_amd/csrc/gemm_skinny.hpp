@@ -264,6 +264,157 @@ __global__ __launch_bounds__(256) void k_qgemm_skinny(const uint8_t* __restrict_
   }
 }
 
+// ------------------------------------------------------- M <= GV_MAX_M rows
+// One activation fragment (rows 0..15, rows past M clamped to M-1: they only
+// feed output rows that are never stored). A block owns 16 weight rows and the
+// whole K range; its GV_NW waves split K by 256-groups (contiguous ranges), so
+// each weight byte is read once and every wave streams two groups ahead. The
+// activation fragments come straight from global memory (the same few rows are
+// read by every block, so they stay in L2); their K order is the weights' (see
+// the lane layout above). The waves' partial sums are added in LDS in wave
+// order (fixed, so the result does not depend on timing) and wave 0 applies the
+// epilogue. No workspace, one launch.
+constexpr int GV_NW = 8;     // waves per block
+constexpr int GV_MAX_M = 8;  // rows up to which k_qgemv is used (measured: from 16 rows on, the
+                             // split-K kernel's shared activation tile wins)
+
+template <int KIND, bool OUT_BF16, bool ACC_OUT>
+__global__ __launch_bounds__(GV_NW * 64) void k_qgemv(const uint8_t* __restrict__ A, int64_t lda_bytes,
+                                                      const uint8_t* __restrict__ B, int64_t ldb,
+                                                      const float* __restrict__ sw, const float* __restrict__ sa,
+                                                      int M, int N, int K, void* __restrict__ C, int64_t ldc,
+                                                      int32_t* __restrict__ acc_out, int64_t ld_acc) {
+  using T = SkTraits<KIND>;
+  constexpr bool I8 = KIND == GEMM_W8A8;
+  constexpr int ALD = I8 ? 4 : 8;  // 16-byte activation loads per lane per group
+  using acc_t = typename std::conditional<I8, i32x4_t, f32x4_t>::type;
+  __shared__ __align__(16) uint8_t red[GV_NW][64][16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int G = K >> 8;
+  const int gpw = (G + GV_NW - 1) / GV_NW;
+  const int gb = min(G, wave * gpw), ge = min(G, gb + gpw);
+  const int ncol = blockIdx.x * 16 + r16;
+  const uint8_t* wrow = B + (int64_t)min(ncol, N - 1) * ldb + 16 * g4;
+  const uint8_t* arow = A + (int64_t)min(r16, M - 1) * lda_bytes;
+
+  struct Stage {
+    u32x4_t w[T::LPG];
+    u32x4_t a[ALD];
+  };
+  auto load = [&](Stage& st, int g) {
+#pragma unroll
+    for (int t = 0; t < T::LPG; ++t)
+      st.w[t] = *reinterpret_cast<const u32x4_t*>(wrow + (int64_t)g * T::WBG + 64 * t);
+    const uint8_t* ag = arow + (int64_t)g * 256 * T::AB;
+#pragma unroll
+    for (int j = 0; j < ALD; ++j) {
+      int elem;  // K index (within the group) of this activation fragment
+      if constexpr (I8) elem = 64 * j + 16 * g4;
+      else if constexpr (KIND == GEMM_W8) elem = 64 * (j >> 1) + 16 * g4 + 8 * (j & 1);
+      else elem = 128 * (j >> 2) + 32 * g4 + 8 * (j & 3);
+      st.a[j] = *reinterpret_cast<const u32x4_t*>(ag + elem * T::AB);
+    }
+  };
+
+  acc_t acc = acc_t{};
+  f32x4_t tot = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Stage& st) {
+    if constexpr (I8) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, st.a[t]),
+                                                    __builtin_bit_cast(i32x4_t, st.w[t]), acc, 0, 0, 0);
+    } else if constexpr (KIND == GEMM_W8) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t lo = h == 0 ? st.w[t].x : st.w[t].z, hi = h == 0 ? st.w[t].y : st.w[t].w;
+          asm volatile("" : "+v"(lo), "+v"(hi));  // keep the code words whole (see k_qgemm_skinny)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, st.a[2 * t + h]),
+                                                        pp_widen_i8x8(lo, hi), acc, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t word = d == 0 ? st.w[t].x : d == 1 ? st.w[t].y : d == 2 ? st.w[t].z : st.w[t].w;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, st.a[4 * t + d]),
+                                                        pp_widen_i4x8(word), acc, 0, 0, 0);
+        }
+    }
+  };
+
+  Stage ring[2];
+  if (gb < ge) load(ring[0], gb);
+  if (gb + 1 < ge) load(ring[1], gb + 1);
+  for (int g = gb; g < ge; g += 2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      if (g + d < ge) {
+        float sg = 0.f;
+        if constexpr (KIND == GEMM_W4) sg = sw[(int64_t)min(ncol, N - 1) * G + g + d];
+        compute(ring[d]);
+        if (g + d + 2 < ge) load(ring[d], g + d + 2);
+        if constexpr (KIND == GEMM_W4) {
+          tot += sg * acc;
+          acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  }
+
+  // Fixed-order sum over the waves, then the epilogue (wave 0).
+  if constexpr (KIND == GEMM_W4)
+    *reinterpret_cast<f32x4_t*>(red[wave][lane]) = tot;
+  else
+    *reinterpret_cast<acc_t*>(red[wave][lane]) = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  acc_t sum = *reinterpret_cast<const acc_t*>(red[0][lane]);
+#pragma unroll
+  for (int w = 1; w < GV_NW; ++w) sum += *reinterpret_cast<const acc_t*>(red[w][lane]);
+  if (ncol >= N) return;
+  const float scol = KIND == GEMM_W4 ? 1.f : sw[ncol];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * g4 + r;
+    if (m >= M) continue;
+    float y;
+    if constexpr (I8) {
+      if constexpr (ACC_OUT) acc_out[(int64_t)m * ld_acc + ncol] = sum[r];
+      y = ((float)sum[r] * sa[m]) * scol;
+    } else {
+      y = sum[r] * scol;
+    }
+    if constexpr (OUT_BF16)
+      reinterpret_cast<__bf16*>(C)[(int64_t)m * ldc + ncol] = (__bf16)y;
+    else
+      reinterpret_cast<float*>(C)[(int64_t)m * ldc + ncol] = y;
+  }
+}
+
+template <int KIND>
+static hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
+  const int64_t lda_bytes = g.lda * (KIND == GEMM_W8A8 ? 1 : 2);
+  const uint8_t* a = (const uint8_t*)g.a;
+  const uint8_t* b = (const uint8_t*)g.b;
+  const dim3 grid((unsigned)((g.n + 15) / 16)), block(GV_NW * 64);
+#define TP_LAUNCH_GV(OB, AO)                                                                                  \
+  hipLaunchKernelGGL((k_qgemv<KIND, OB, AO>), grid, block, 0, stream, a, lda_bytes, b, g.ldb, g.w_scales,    \
+                     g.a_scales, (int)g.m, (int)g.n, (int)g.k, g.c, g.ldc, g.acc_out, g.ld_acc)
+  if (KIND == GEMM_W8A8 && g.acc_out) {
+    if (g.c_bf16) TP_LAUNCH_GV(true, true); else TP_LAUNCH_GV(false, true);
+  } else {
+    if (g.c_bf16) TP_LAUNCH_GV(true, false); else TP_LAUNCH_GV(false, false);
+  }
+#undef TP_LAUNCH_GV
+  return hipGetLastError();
+}
+
 // Sum of the split partials in split order, then the epilogue. One thread per
 // output element; blockIdx.y is the row.
 template <int KIND, bool OUT_BF16, bool ACC_OUT>
@@ -295,8 +446,10 @@ __global__ __launch_bounds__(256) void k_qgemm_reduce(const void* __restrict__ p
     reinterpret_cast<float*>(C)[(int64_t)m * ldc + n] = y;
 }
 
-// Launch plan of the small-M path for one product shape.
+// Launch plan of the small-M path for one product shape (splits == 1: no
+// partial sums in the workspace).
 struct SkPlan {
+  bool gemv;   // M <= GV_MAX_M: k_qgemv (one launch, no partial sums)
   int fm;      // 16-row activation fragments per block (1, 2 or 4)
   int mb;      // blocks along M
   int nb;      // blocks along N
@@ -311,6 +464,10 @@ constexpr int SK_MAX_LDS = 64 * 1024;  // activation stage per block (the defaul
 
 inline bool skinny_plan(int kind, int64_t m, int64_t n, int64_t k, SkPlan* p) {
   if (m < 1 || m > SK_MAX_M || n < 1 || k < 256) return false;
+  if (m <= GV_MAX_M) {
+    *p = SkPlan{true, 1, 1, (int)((n + 15) / 16), 1, (int)(k / 256), 0};
+    return (n + 15) / 16 <= INT32_MAX;
+  }
   const int fm = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
   const int mr = 16 * fm;
   const int ab = kind == GEMM_W8A8 ? 1 : 2;
@@ -327,6 +484,7 @@ inline bool skinny_plan(int kind, int64_t m, int64_t n, int64_t k, SkPlan* p) {
   if (gps > gmax) gps = gmax;
   splits = (G + gps - 1) / gps;
   if (base * splits > INT32_MAX) return false;
+  p->gemv = false;
   p->fm = fm;
   p->mb = (int)mb;
   p->nb = (int)nb;
@@ -373,6 +531,7 @@ static hipError_t launch_skinny_fm(const GemmArgs& g, const SkPlan& p, hipStream
 
 template <int KIND>
 static hipError_t launch_skinny(const GemmArgs& g, const SkPlan& p, hipStream_t stream) {
+  if (p.gemv) return launch_gemv<KIND>(g, stream);
   switch (p.fm) {
     case 1: return launch_skinny_fm<KIND, 1>(g, p, stream);
     case 2: return launch_skinny_fm<KIND, 2>(g, p, stream);

@@ -176,7 +176,7 @@ def w8a8(lib, a=A, ad=1, lda=512, flags=1, q=B, ldq=512, s=C, m=64, n=256, k=512
     (dict(c=B), 10),                                 # c overlaps q
     (dict(flags=-1), 11),
     (dict(qa=0x30000000, sa=0x30000000 + 64 * 512 - 4), 10),
-    (dict(m=16, qa=0x30000000, sa=0x38000000, ws=0, wsb=0), 9),   # split-K partial sums still need room
+    (dict(m=40, qa=0x30000000, sa=0x38000000, ws=0, wsb=0), 9),   # split-K partial sums still need room
 ])
 def test_w8a8_refusals(lib, kw, status):
     assert w8a8(lib, **kw) == status, _err(lib)
@@ -187,12 +187,15 @@ def test_w8a8_own_codes_need_no_workspace(lib):
 
 
 def test_small_m_workspace_refusals(lib):
-    # a pre-rotated small-M product still needs room for its partial sums
-    assert w8(lib, flags=0, m=16, ws=0, wsb=0) == 9
-    need = lib.tp_workspace_size(1, 16, 256, 512, 0)
+    # a pre-rotated product with 17..64 rows still needs room for its split-K
+    # partial sums; up to 8 rows it needs none (single-launch kernel)
+    assert w8(lib, flags=0, m=40, ws=0, wsb=0) == 9
+    need = lib.tp_workspace_size(1, 40, 256, 512, 0)
     assert need > 0
-    assert w8(lib, flags=0, m=16, wsb=need - 1) == 9
-    assert w8(lib, flags=0, m=16, ws=E + 8, wsb=need) == 5
+    assert w8(lib, flags=0, m=40, wsb=need - 1) == 9
+    assert w8(lib, flags=0, m=40, ws=E + 8, wsb=need) == 5
+    assert lib.tp_workspace_size(1, 8, 12288, 3072, 0) == 0
+    assert lib.tp_workspace_size(4, 1, 24576, 3072, 0) == 0
 
 
 def pq(lib, qa=A, ldqa=512, sa=C, q=B, ldq=512, s=C + 4096, m=64, n=256, k=512, c=D, cd=0, ldc=256, acc=0, ld_acc=0,
@@ -242,7 +245,7 @@ def test_workspace_sizes_small_m(lib):
     front = (m * k + 255) // 256 * 256 + 4 * m
     assert lib.tp_workspace_size(3, m, n, k, 1) == (front + 255) // 256 * 256 + w8a8_pre
     # one 256-group cannot be split
-    assert lib.tp_workspace_size(1, 1, 256, 256, 0) == 0
+    assert lib.tp_workspace_size(1, 40, 256, 256, 0) == 0
     # above the small-M range nothing but the front part
     assert lib.tp_workspace_size(1, 65, n, k, 0) == 0
     assert lib.tp_workspace_size(1, 3, 9, 255, 0) == 0

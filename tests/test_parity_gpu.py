@@ -351,8 +351,9 @@ def _small_m_case(kind, wl, rows=None, out_dtype=torch.float32):
 
 
 @pytest.mark.parametrize("kind", ["w8", "w4", "w8a8"])
-@pytest.mark.parametrize("m,n,k", [(1, 300, 512), (5, 1000, 2560), (16, 129, 256), (17, 777, 1536),
-                                   (33, 4000, 768), (64, 515, 3072), (64, 128, 12288)])
+@pytest.mark.parametrize("m,n,k", [(1, 300, 512), (5, 1000, 2560), (8, 4100, 3840), (9, 333, 1280),
+                                   (16, 129, 256), (17, 777, 1536), (33, 4000, 768), (64, 515, 3072),
+                                   (64, 128, 12288), (3, 20, 12288)])
 def test_small_m_ragged(kind, m, n, k):
     """Few-row products: split-K with several 256-groups per split, ragged N,
     M not a multiple of 16, a single 256-group (no split)."""
@@ -364,7 +365,7 @@ def test_small_m_ragged(kind, m, n, k):
 
 @pytest.mark.parametrize("name,kind", [("ffn_up", "w8"), ("ffn_down", "w4"), ("dit_qkv", "w8a8"),
                                        ("dit_gateup", "w8a8")])
-@pytest.mark.parametrize("rows", [1, 16, 64])
+@pytest.mark.parametrize("rows", [1, 8, 16, 64])
 def test_small_m_full_weights(name, kind, rows):
     """The first rows of the full-size workloads against their full weights
     (the M <= 64 sweep the benchmark times), every output element."""
