@@ -284,20 +284,28 @@ static hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Kernel table. Outputs with at least 128 tiles of 256x256 (every
-// diffusion-block projection at M = 4096) run the two-group multi-stage kernel
-// of gemm_pp.hpp: 256x256 tiles of 8 waves (128x64 each) for W8 and W8A8,
-// 256x128 tiles (128x32 each) for W4, whose per-group fold needs a second set
-// of accumulators. Smaller outputs use the single-stage kernels above with
-// 128x128 tiles, so that the 256 CUs still get several tiles each. Chosen from
-// measured sweeps on MI355X.
-enum KernelCfg { CFG_SMALL_128 = 0, CFG_PP_256x256 = 1, CFG_PP_256x128 = 2 };
+// Kernel table (from measured sweeps on MI355X). Outputs with at least 128
+// tiles of 256x256 run the two-group multi-stage kernel of gemm_pp.hpp:
+//   W8     256x256 tiles of 8 waves (128x64 each), 3 stages;
+//   W8A8   256x256 (128x64 waves), 4 stages; 256x192 (64x96 waves) when the
+//          256x256 grid would leave CUs idle and the 192-wide one does not
+//          (e.g. N = 3072 at M = 4096: 192 -> 256 tiles for 256 CUs);
+//   W4     128x192 tiles (64x48 waves), 5 stages: the per-group fold keeps a
+//          second set of accumulators, which bounds the wave tile, and the
+//          4032x3072 product splits into 512 tiles (two full rounds) instead
+//          of 384 (1.5 rounds) for 256x128.
+// Smaller outputs use the single-stage kernels above with 128x128 tiles, so
+// that the 256 CUs still get several tiles each.
+enum KernelCfg { CFG_SMALL_128 = 0, CFG_PP_256x256 = 1, CFG_PP_128x192 = 2, CFG_PP_256x192 = 3 };
+constexpr int64_t NUM_CUS = 256;
 
 static int pick_cfg(int kind, int64_t m, int64_t n, int64_t k) {
   (void)k;
   const int64_t big = ((m + 255) / 256) * ((n + 255) / 256);
   if (big < 128) return CFG_SMALL_128;
-  return kind == GEMM_W4 ? CFG_PP_256x128 : CFG_PP_256x256;
+  if (kind == GEMM_W4) return CFG_PP_128x192;
+  if (kind == GEMM_W8A8 && big < NUM_CUS && ((m + 255) / 256) * ((n + 191) / 192) <= NUM_CUS) return CFG_PP_256x192;
+  return CFG_PP_256x256;
 }
 
 void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn) {
@@ -309,7 +317,8 @@ void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn)
   }
   switch (pick_cfg(kind, m, n, k)) {
     case CFG_PP_256x256: *bm = 256; *bn = 256; return;
-    case CFG_PP_256x128: *bm = 256; *bn = 128; return;
+    case CFG_PP_128x192: *bm = 128; *bn = 192; return;
+    case CFG_PP_256x192: *bm = 256; *bn = 192; return;
     default: *bm = 128; *bn = 128; return;
   }
 }
@@ -334,8 +343,11 @@ static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
       if constexpr (KIND == GEMM_W8A8) return launch_pp<KIND, 256, 256, 128, 64, 4>(g, stream);
       if constexpr (KIND == GEMM_W8) return launch_pp<KIND, 256, 256, 128, 64, 3>(g, stream);
       break;
-    case CFG_PP_256x128:
-      if constexpr (KIND == GEMM_W4) return launch_pp<KIND, 256, 128, 128, 32, 3>(g, stream);
+    case CFG_PP_128x192:
+      if constexpr (KIND == GEMM_W4) return launch_pp<KIND, 128, 192, 64, 48, 5>(g, stream);
+      break;
+    case CFG_PP_256x192:
+      if constexpr (KIND == GEMM_W8A8) return launch_pp<KIND, 256, 192, 64, 96, 4>(g, stream);
       break;
     default: break;
   }
