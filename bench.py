@@ -52,6 +52,10 @@ def parse():
     p.add_argument("--cpu-only", action="store_true", help="time only the CPU oracle sample (no GPU)")
     p.add_argument("--small-m", action="store_true",
                    help="instead of the step: the M <= 64 HBM-bound sweep (one JSON line per case)")
+    p.add_argument("--only", default=None,
+                   help="run only the launches whose name contains this text (for counter profiling)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                   help="before the step, run a plain device copy of MB MiB (a kernel of known traffic)")
     return p.parse_args()
 
 
@@ -62,10 +66,15 @@ def step_plan():
 
 
 def _src_hash():
+    """Hash of every kernel source: a committed counter profile applies only
+    to the kernels it was taken on."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "rotate.hip", "device_common.hpp"):
-        with open(os.path.join(ROOT, "int4_quantized_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    d = os.path.join(ROOT, "int4_quantized_gemm_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode())
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -272,6 +281,17 @@ def main():
                              lambda e=e, fn=fn: fn(e["xr"], e["q"], e["s"], rotate=False, out=e["out"],
                                                    workspace=ws)))
     step_ops = sum(u for _, k, u, _ in launches if k != "hbm")
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 2 ** 20 // 4
+        src = torch.ones((n,), dtype=torch.float32, device=d)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # one elementwise kernel: n*4 B read, n*4 B written
+        torch.cuda.synchronize()
+        del src, dst
+    if args.only:
+        launches = [l for l in launches if args.only in l[0]]
+        assert launches, f"no launch matches {args.only!r}"
 
     def run_step(events=None):
         for i, (_, _, _, fn) in enumerate(launches):
