@@ -49,14 +49,13 @@ namespace tp {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Block -> tile map: each of the 8 XCDs owns one contiguous range of logical
-// tiles (hardware deals blocks round-robin over XCDs), walked in groups of 8
+// tiles (hardware deals blocks round-robin over XCDs), walked in groups of GM
 // tile-rows so that blocks resident together on one XCD share A rows and B
 // columns in that XCD's L2.
-__device__ __forceinline__ void pp_map_tile(int pid, int nblk, int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ void pp_map_tile(int pid, int nblk, int tiles_m, int tiles_n, int GM, int& tm, int& tn) {
   const int q = nblk >> 3, r = nblk & 7;
   const int xcd = pid & 7, idx = pid >> 3;
   const int logical = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-  constexpr int GM = 8;
   const int width = GM * tiles_n;
   const int group = logical / width;
   const int first_m = group * GM;
@@ -111,7 +110,7 @@ template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE, bool OUT_BF16, b
 __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
     const uint8_t* __restrict__ A, int64_t lda_bytes, const uint8_t* __restrict__ B, int64_t ldb_bytes,
     const float* __restrict__ sw, const float* __restrict__ sa, int M, int N, int K, void* __restrict__ Cv,
-    int64_t ldc, int32_t* __restrict__ acc_out, int64_t ld_acc, int tiles_m, int tiles_n) {
+    int64_t ldc, int32_t* __restrict__ acc_out, int64_t ld_acc, int tiles_m, int tiles_n, int gm) {
   using Cfg = PPCfg<KIND, BM, BN, WM, WN, NSTAGE>;
   constexpr bool I8 = Cfg::I8;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, NWN = Cfg::NWN;
@@ -121,7 +120,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   __shared__ __align__(1024) uint8_t ring[Cfg::LDS_BYTES];
 
   int tm, tn;
-  pp_map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  pp_map_tile(blockIdx.x, gridDim.x, tiles_m, tiles_n, gm, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -401,7 +400,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
 }
 
 template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE>
-static hipError_t launch_pp(const GemmArgs& g, hipStream_t stream) {
+static hipError_t launch_pp(const GemmArgs& g, hipStream_t stream, int gm = 8) {
   const int tiles_m = (int)((g.m + BM - 1) / BM), tiles_n = (int)((g.n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(512);
   const int64_t lda_bytes = g.lda * (KIND == GEMM_W8A8 ? 1 : 2);
@@ -410,7 +409,7 @@ static hipError_t launch_pp(const GemmArgs& g, hipStream_t stream) {
 #define TP_LAUNCH_PP(OB, AO)                                                                                   \
   hipLaunchKernelGGL((k_qgemm_pp<KIND, BM, BN, WM, WN, NSTAGE, OB, AO>), grid, block, 0, stream, a, lda_bytes, b, \
                      g.ldb, g.w_scales, g.a_scales, (int)g.m, (int)g.n, (int)g.k, g.c, g.ldc, g.acc_out, g.ld_acc, \
-                     tiles_m, tiles_n)
+                     tiles_m, tiles_n, gm)
   if (KIND == GEMM_W8A8 && g.acc_out) {
     if (g.c_bf16) TP_LAUNCH_PP(true, true); else TP_LAUNCH_PP(false, true);
   } else {
