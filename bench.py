@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--cpu-only", action="store_true", help="time only the CPU oracle sample (no GPU)")
     p.add_argument("--small-m", action="store_true",
                    help="instead of the step: the M <= 64 HBM-bound sweep (one JSON line per case)")
+    p.add_argument("--library-reference", action="store_true",
+                   help="instead of the step: time the platform's own int8 / bf16 GEMMs (hipBLASLt through torch) on "
+                        "the step's shapes, as context for the roofline fractions (one JSON line per shape)")
     p.add_argument("--only", default=None,
                    help="run only the launches whose name contains this text (for counter profiling)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -213,6 +216,49 @@ def small_m_sweep(args):
         torch.cuda.empty_cache()
 
 
+# ------------------------------------------- platform library, for context only
+def library_reference(args):
+    """The platform's own GEMMs on the step's shapes: torch._int_mm (int8 x
+    int8 -> int32) for the W8A8 products and a bf16 matmul for the
+    weight-only ones. Plain products without rotation, quantization or scale
+    epilogue; a measure of what the vendor library reaches on this GPU, not a
+    part of the product path."""
+    import statistics
+    import torch
+    d = torch.device("cuda:0")
+
+    def timed(f, reps=20):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        res = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) / reps * 1e-3)
+        return statistics.median(res)
+
+    for kind, wl in step_plan():
+        m, k, n = wl.m, wl.k, wl.n
+        if kind == "w8a8":
+            a = torch.randint(-127, 128, (m, k), dtype=torch.int8, device=d)
+            b = torch.randint(-127, 128, (n, k), dtype=torch.int8, device=d).t()
+            f, what, peak = (lambda: torch._int_mm(a, b)), "torch._int_mm int8->int32", PEAK_TOPS_I8
+        else:
+            a = torch.randn((m, k), device=d).to(torch.bfloat16)
+            b = torch.randn((n, k), device=d).to(torch.bfloat16).t()
+            f, what, peak = (lambda: a @ b), "torch.matmul bf16", PEAK_TFLOPS_BF16
+        sec = timed(f)
+        rate = 2.0 * m * n * k / sec / 1e12
+        print(json.dumps({"metric": "platform library GEMM (context)", "shape": wl.name, "m": m, "k": k, "n": n,
+                          "op": what, "us": round(sec * 1e6, 1), "rate": round(rate, 1),
+                          "frac_of_peak": round(rate / peak, 4)}), flush=True)
+
+
 # ------------------------------------------------------------------ GPU path
 def main():
     args = parse()
@@ -225,6 +271,9 @@ def main():
         return
     if args.small_m:
         small_m_sweep(args)
+        return
+    if args.library_reference:
+        library_reference(args)
         return
 
     import torch
