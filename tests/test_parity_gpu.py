@@ -185,6 +185,34 @@ def test_quantize_rows_zero_and_tiny_rows():
     assert host(sa)[1] == 0 and np.all(host(qa)[1] == 0)
 
 
+@pytest.mark.parametrize("k", [3072, 12288])
+def test_quantize_rows_exact_ties(k):
+    """Every rotated value is a half-integer multiple of a power-of-two scale,
+    so every code is a rounding tie: the device must round half to even, as
+    the reference rule does (the fp32 bound cannot decide any of them, so each
+    goes through the exact recomputation). Rotated (fp32 input) and
+    pre-rotated (bf16 input) paths."""
+    d = dev()
+    announce("tp_quantize_rows_int8 exact ties", k)
+    rng = np.random.default_rng(40 + k)
+    m, c = 24, 2.0 ** -3
+    xr = (rng.integers(-127, 127, size=(m, k)) + 0.5) * c      # rotated values: (j + 1/2) c
+    xr[:, 17] = 127 * c                                          # the row maximum: s = c exactly
+    xr[3] = 0.5 * c                                              # a row of 1/2 ties (all -> 0)
+    xr[3, 0] = 127 * c
+    H = oracle.hadamard_matrix(256) / 16.0
+    unrot = lambda a: np.concatenate([a[:, g * 256:(g + 1) * 256] @ H for g in range(k // 256)], axis=1)
+    x = torch.from_numpy(unrot(xr).astype(np.float32))
+    assert np.array_equal(oracle.rotate_groups(x.numpy()), xr)  # exact in fp32
+    expect = np.rint(xr / c).astype(np.int8)                    # numpy rint: half to even
+    for inp, rotate in ((x, True), (torch.from_numpy(xr.astype(np.float32)).to(torch.bfloat16), False)):
+        qa, sa = tp.tp_quantize_rows_int8(inp.to(d), rotate=rotate)
+        rqa, rsa = oracle.quantize_activations_int8(f64(inp), rotate=rotate)
+        assert np.all(host(sa) == np.float32(c)) and np.array_equal(rsa, host(sa))
+        assert np.array_equal(rqa, expect)
+        assert np.array_equal(host(qa), expect), f"{int(np.sum(host(qa) != expect))} tie codes differ"
+
+
 # ------------------------------------------------------------- W8 / W4 products
 def _w8_case(wl, row_sel=None, out_dtype=None):
     d = dev()
