@@ -46,6 +46,10 @@
 
 namespace tp {
 
+// Fixed-order sum of split-K partial sums plus the epilogue (gemm_skinny.hpp).
+template <int KIND>
+static hipError_t launch_reduce(const GemmArgs& g, int splits, hipStream_t stream);
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Block -> tile map: each of the 8 XCDs owns one contiguous range of logical
@@ -106,11 +110,17 @@ struct PPCfg {
   static_assert(LPW * (NSTAGE - 2) < 64, "vmcnt range");
 };
 
-template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE, bool OUT_BF16, bool ACC_OUT>
+// PARTIAL: the block computes the K stages [blockIdx.y * sps, ...) of its
+// tile and writes the raw sums (int32 for W8A8, unscaled fp32 for W8, folded
+// fp32 for W4) to part[blockIdx.y][m][n] instead of C; k_qgemm_reduce adds the
+// splits in order and applies the epilogue. sps is a multiple of 4 (whole
+// 256-groups).
+template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE, bool OUT_BF16, bool ACC_OUT, bool PARTIAL>
 __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
     const uint8_t* __restrict__ A, int64_t lda_bytes, const uint8_t* __restrict__ B, int64_t ldb_bytes,
     const float* __restrict__ sw, const float* __restrict__ sa, int M, int N, int K, void* __restrict__ Cv,
-    int64_t ldc, int32_t* __restrict__ acc_out, int64_t ld_acc, int tiles_m, int tiles_n, int gm) {
+    int64_t ldc, int32_t* __restrict__ acc_out, int64_t ld_acc, int tiles_m, int tiles_n, int gm, int sps,
+    void* __restrict__ part) {
   using Cfg = PPCfg<KIND, BM, BN, WM, WN, NSTAGE>;
   constexpr bool I8 = Cfg::I8;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, NWN = Cfg::NWN;
@@ -160,7 +170,10 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
       kbytes[i] = BROW;
     }
   }
-  const int KS = K >> 6;  // stages of 64 K
+  const int ks0 = PARTIAL ? blockIdx.y * sps : 0;             // first stage of this block's K range
+  const int KS = PARTIAL ? min(sps, (K >> 6) - ks0) : K >> 6;  // stages of 64 K in the range
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) src[i] += (int64_t)ks0 * kbytes[i];
   auto issue_stage = [&](int ks) {
     uint8_t* base = ring + (ks % NSTAGE) * STAGE;
 #pragma unroll
@@ -218,7 +231,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
     }
     if constexpr (KIND == GEMM_W4) {
       if ((ks & 3) == 3) {  // last stage of a 256-group: fetch the group's scales for the fold
-        const int g = ks >> 2;
+        const int g = (ks0 + ks) >> 2;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = min(n0 + wn0 + j * 16 + r16, N - 1);
@@ -299,11 +312,11 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   // between stores would drain every store before it).
   float ep_sw[KIND == GEMM_W4 ? 1 : FN];
   float ep_sa[KIND == GEMM_W8A8 ? FM : 1][4];
-  if constexpr (KIND != GEMM_W4) {
+  if constexpr (KIND != GEMM_W4 && !PARTIAL) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) ep_sw[j] = sw[min(n0 + wn0 + j * 16 + r16, N - 1)];
   }
-  if constexpr (KIND == GEMM_W8A8) {
+  if constexpr (KIND == GEMM_W8A8 && !PARTIAL) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -352,6 +365,30 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   }
   if (grp == 0) barrier_only();
 
+  if constexpr (PARTIAL) {
+    // Raw sums of this K range, [split][m][n] with row pitch N.
+    __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(0));
+    typedef typename std::conditional<KIND == GEMM_W8A8, int32_t, float>::type part_t;
+    part_t* pbase = reinterpret_cast<part_t*>(part) + (int64_t)blockIdx.y * M * N;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm0 + i * 16 + g4 * 4 + r;
+        if (row >= M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + wn0 + j * 16 + r16;
+          if (col >= N) continue;
+          if constexpr (KIND == GEMM_W4)
+            pbase[(int64_t)row * N + col] = tot[i][j][r];
+          else
+            pbase[(int64_t)row * N + col] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+
   // Epilogue: lane l of a 16x16 tile holds rows 4*(l/16)+r, column l%16.
   // Every load this wave issued has completed here; waiting once up front
   // keeps the compiler from re-waiting on the preloaded scales between
@@ -399,21 +436,29 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   }
 }
 
+// splits > 1: K split over blockIdx.y into ranges of sps stages, partial sums
+// in g.part, then k_qgemm_reduce (gemm_skinny.hpp).
 template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE>
-static hipError_t launch_pp(const GemmArgs& g, hipStream_t stream, int gm = 8) {
+static hipError_t launch_pp(const GemmArgs& g, hipStream_t stream, int gm = 8, int splits = 1, int sps = 0) {
   const int tiles_m = (int)((g.m + BM - 1) / BM), tiles_n = (int)((g.n + BN - 1) / BN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(512);
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(512);
   const int64_t lda_bytes = g.lda * (KIND == GEMM_W8A8 ? 1 : 2);
   const uint8_t* a = (const uint8_t*)g.a;
   const uint8_t* b = (const uint8_t*)g.b;
-#define TP_LAUNCH_PP(OB, AO)                                                                                   \
-  hipLaunchKernelGGL((k_qgemm_pp<KIND, BM, BN, WM, WN, NSTAGE, OB, AO>), grid, block, 0, stream, a, lda_bytes, b, \
-                     g.ldb, g.w_scales, g.a_scales, (int)g.m, (int)g.n, (int)g.k, g.c, g.ldc, g.acc_out, g.ld_acc, \
-                     tiles_m, tiles_n, gm)
+#define TP_LAUNCH_PP(OB, AO, PA)                                                                                  \
+  hipLaunchKernelGGL((k_qgemm_pp<KIND, BM, BN, WM, WN, NSTAGE, OB, AO, PA>), grid, block, 0, stream, a, lda_bytes, b, \
+                     g.ldb, g.w_scales, g.a_scales, (int)g.m, (int)g.n, (int)g.k, g.c, g.ldc, g.acc_out, g.ld_acc,    \
+                     tiles_m, tiles_n, gm, sps, g.part)
+  if (splits > 1) {
+    TP_LAUNCH_PP(false, false, true);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_reduce<KIND>(g, splits, stream);
+  }
   if (KIND == GEMM_W8A8 && g.acc_out) {
-    if (g.c_bf16) TP_LAUNCH_PP(true, true); else TP_LAUNCH_PP(false, true);
+    if (g.c_bf16) TP_LAUNCH_PP(true, true, false); else TP_LAUNCH_PP(false, true, false);
   } else {
-    if (g.c_bf16) TP_LAUNCH_PP(true, false); else TP_LAUNCH_PP(false, false);
+    if (g.c_bf16) TP_LAUNCH_PP(true, false, false); else TP_LAUNCH_PP(false, false, false);
   }
 #undef TP_LAUNCH_PP
   return hipGetLastError();

@@ -516,9 +516,14 @@ static hipError_t launch_skinny_fm(const GemmArgs& g, const SkPlan& p, hipStream
   if (!split) return hipGetLastError();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_reduce<KIND>(g, p.splits, stream);
+}
+
+template <int KIND>
+static hipError_t launch_reduce(const GemmArgs& g, int splits, hipStream_t stream) {
   const dim3 rgrid((unsigned)((g.n + 255) / 256), (unsigned)g.m), rblock(256);
 #define TP_LAUNCH_RED(OB, AO)                                                                                     \
-  hipLaunchKernelGGL((k_qgemm_reduce<KIND, OB, AO>), rgrid, rblock, 0, stream, g.part, p.splits, (int)g.m,        \
+  hipLaunchKernelGGL((k_qgemm_reduce<KIND, OB, AO>), rgrid, rblock, 0, stream, g.part, splits, (int)g.m,          \
                      (int)g.n, g.w_scales, g.a_scales, g.c, g.ldc, g.acc_out, g.ld_acc)
   if (KIND == GEMM_W8A8 && g.acc_out) {
     if (g.c_bf16) TP_LAUNCH_RED(true, true); else TP_LAUNCH_RED(false, true);

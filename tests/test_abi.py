@@ -246,8 +246,11 @@ def test_workspace_sizes_small_m(lib):
     assert lib.tp_workspace_size(3, m, n, k, 1) == (front + 255) // 256 * 256 + w8a8_pre
     # one 256-group cannot be split
     assert lib.tp_workspace_size(1, 40, 256, 256, 0) == 0
-    # above the small-M range nothing but the front part
-    assert lib.tp_workspace_size(1, 65, n, k, 0) == 0
+    # above the small-M range: split-K partial sums only while the output has
+    # fewer than 128 tiles of 256x256; large outputs need nothing
+    mid = lib.tp_workspace_size(1, 65, n, k, 0)
+    assert mid > 0 and mid % (4 * 65 * n) == 0
+    assert lib.tp_workspace_size(1, 4096, n, k, 0) == 0
     assert lib.tp_workspace_size(1, 3, 9, 255, 0) == 0
 
 

@@ -424,6 +424,7 @@ def test_small_m_bf16_out_and_views():
 
 
 @pytest.mark.parametrize("kind,m,n,k", [("w8a8", 4000, 9000, 768), ("w8a8", 3000, 2900, 512), ("w8", 4000, 8000, 512),
+                                        ("w4", 300, 3000, 4096), ("w8a8", 500, 1000, 6144), ("w8", 1000, 700, 2048),
                                         ("w4", 4000, 8000, 1024), ("w8a8", 2100, 9000, 256)])
 def test_multistage_path_ragged(kind, m, n, k):
     """Shapes large enough for the 256-wide multi-stage kernels, with M and N
