@@ -3,7 +3,7 @@
 // gemm_skinny.hpp (few activation rows).
 //
 //   W8    C = (bf16(A') . q^T) * s[n]            bf16 MFMA 16x16x32, fp32 sums
-//   W4    C = sum_g s[n,g] * (bf16(A'_g) . q_g^T) bf16 MFMA, per-group fp32 fold
+//   W4    C = sum_g s[n,g] * (bf16(A'_g) . q_g^T) bf16 MFMA, per-group fp32 rescale
 //   W8A8  acc = qa . q^T (int32, exact); C = (float(acc) * sa[m]) * sw[n]
 //                                                 i8 MFMA 16x16x64, int32 sums
 //
@@ -31,15 +31,17 @@ namespace tp {
 //   W8A8   256x256 (128x64 waves), 4 stages; 256x192 (64x96 waves) when the
 //          256x256 grid would leave CUs idle and the 192-wide one does not
 //          (e.g. N = 3072 at M = 4096: 192 -> 256 tiles for 256 CUs);
-//   W4     128x192 tiles (64x48 waves), 5 stages: the per-group fold keeps a
-//          second set of accumulators, which bounds the wave tile, and the
-//          4032x3072 product splits into 512 tiles (two full rounds) instead
-//          of 384 (1.5 rounds) for 256x128.
+//   W4     256x192 (128x48 waves), 3 stages, when that grid has at least 192
+//          tiles (4032x3072 splits into exactly 256): 128-row waves spread
+//          the widening of each code over 8 MFMAs (measured 4032x3072x12288:
+//          391 us with 64x48 waves and a second accumulator set, 277 us);
+//          below that, 128x192 (64x48 waves, 5 stages).
 // The last launch argument is the number of tile-rows an XCD walks together
 // (pp_map_tile): 4 for W8, W4 and wide W8A8 outputs, 8 otherwise (measured:
 // W8 4096x3072x12288 307 -> 257 us from 8 to 4).
 // Smaller outputs: see pick_plan.
 enum KernelCfg { CFG_PP_256x256 = 1, CFG_PP_128x192 = 2, CFG_PP_256x192 = 3 };
+constexpr int64_t W4_MIN_WIDE_TILES = 192;
 constexpr int64_t NUM_CUS = 256;
 
 struct PpPlan {
@@ -53,6 +55,8 @@ struct PpPlan {
 // splits' partial sums go to the workspace and k_qgemm_reduce adds them.
 static PpPlan pick_plan(int kind, int64_t m, int64_t n, int64_t k) {
   const int64_t big = ((m + 255) / 256) * ((n + 255) / 256);
+  if (kind == GEMM_W4 && ((m + 255) / 256) * ((n + 191) / 192) >= W4_MIN_WIDE_TILES)
+    return PpPlan{CFG_PP_256x192, 1, 0};
   if (big >= 128) {
     if (kind == GEMM_W4) return PpPlan{CFG_PP_128x192, 1, 0};
     if (kind == GEMM_W8A8 && big < NUM_CUS && ((m + 255) / 256) * ((n + 191) / 192) <= NUM_CUS)
@@ -116,6 +120,7 @@ static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
       break;
     case CFG_PP_256x192:
       if constexpr (KIND == GEMM_W8A8) return launch_pp<KIND, 256, 192, 64, 96, 4>(g, stream);
+      if constexpr (KIND == GEMM_W4) return launch_pp<KIND, 256, 192, 128, 48, 3>(g, stream, 4);
       break;
     default:
       return launch_pp<KIND, 128, 192, 64, 48, 5>(g, stream, 4, pl.splits, pl.sps);

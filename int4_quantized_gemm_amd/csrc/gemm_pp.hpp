@@ -2,7 +2,7 @@
 // schedule over a multi-stage LDS ring.
 //
 //   W8    C = (bf16(A') . q^T) * s[n]              bf16 MFMA 16x16x32, fp32 sums
-//   W4    C = sum_g s[n,g] * (bf16(A'_g) . q_g^T)  bf16 MFMA, per-group fp32 fold
+//   W4    C = sum_g s[n,g] * (bf16(A'_g) . q_g^T)  bf16 MFMA, per-group fp32 rescale
 //   W8A8  acc = qa . q^T (int32, exact); C = (float(acc) * sa[m]) * sw[n]
 //                                                   i8 MFMA 16x16x64, int32 sums
 //
@@ -37,6 +37,12 @@
 // group g = lane/16 the K positions 16g + 8kk + [0, 8); A and B use the same
 // order, so one 16-byte int8 (8-byte int4) weight read serves both k-steps.
 // The i8 kind has one k-step per stage: 16g + [0, 16).
+//
+// W4 widening: one masked AND per 8 codes moves each code to the top nibble of
+// a byte and a signed-byte convert gives 16 * code, so the MFMAs sum 16x the
+// products (exact in bf16 and removed by an exact 1/16 at the end). The group
+// scales are applied by rescaling the single set of accumulators at group
+// boundaries (see cu in the kernel).
 #pragma once
 
 #include <type_traits>
@@ -90,6 +96,21 @@ __device__ __forceinline__ bf16x8_t pp_widen_i4x8(uint32_t w) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
+// 8 int4 codes (one dword, code j in bits 4j..4j+3) -> 8 bf16 holding 16 *
+// code, exact. Each code is moved to the top nibble of a byte, so a signed
+// byte convert (one SDWA instruction) yields 16 * code. mk is 0xF0F0F0F0, or
+// 0 to drop the codes of a group that does not take part.
+__device__ __forceinline__ bf16x8_t pp_widen_i4x8_x16(uint32_t w, uint32_t mk) {
+  const uint32_t hi = w & mk;         // byte j: code 2j+1 in the top nibble
+  const uint32_t lo = (w << 4) & mk;  // byte j: code 2j in the top nibble
+  u32x4_t o;
+  o.x = pack_bf16x2((float)(int8_t)(lo), (float)(int8_t)(hi));
+  o.y = pack_bf16x2((float)(int8_t)(lo >> 8), (float)(int8_t)(hi >> 8));
+  o.z = pack_bf16x2((float)(int8_t)(lo >> 16), (float)(int8_t)(hi >> 16));
+  o.w = pack_bf16x2((float)(int8_t)(lo >> 24), (float)(int8_t)(hi >> 24));
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
 template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE>
 struct PPCfg {
   static constexpr bool I8 = KIND == GEMM_W8A8;
@@ -111,7 +132,7 @@ struct PPCfg {
 };
 
 // PARTIAL: the block computes the K stages [blockIdx.y * sps, ...) of its
-// tile and writes the raw sums (int32 for W8A8, unscaled fp32 for W8, folded
+// tile and writes the raw sums (int32 for W8A8, unscaled fp32 for W8, scaled
 // fp32 for W4) to part[blockIdx.y][m][n] instead of C; k_qgemm_reduce adds the
 // splits in order and applies the epilogue. sps is a multiple of 4 (whole
 // 256-groups).
@@ -188,13 +209,16 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
-  f32x4_t tot[KIND == GEMM_W4 ? FM : 1][KIND == GEMM_W4 ? FN : 1];
-  if constexpr (KIND == GEMM_W4) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) tot[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  // W4 keeps one accumulator per output, expressed in units of the scale of
+  // the group being summed (cu, per column): the raw products of group g are
+  // added as they come, and on entering group g+1 the accumulator is
+  // multiplied by s[g]/s[g+1]. A group whose scale is zero, or more than 2^64
+  // times smaller than the running unit (where the rescale could overflow),
+  // has its codes masked off; a column with a skipped nonzero scale is
+  // recomputed exactly in the epilogue (fix bit).
+  float cu[KIND == GEMM_W4 ? FN : 1];
+  uint32_t mk[KIND == GEMM_W4 ? FN : 1];
+  int fix = 0;
 
   const int r16 = lane & 15, g4 = lane >> 4;
   const int groups = K >> 8;
@@ -205,7 +229,25 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   u32x4_t fa[NKK][FM];
   typedef typename std::conditional<KIND == GEMM_W4, uint2, u32x4_t>::type braw_t;
   braw_t fb[FN];
-  float s_grp[KIND == GEMM_W4 ? FN : 1];  // W4: scales of the group being folded
+  float s_nx[KIND == GEMM_W4 ? FN : 1];  // W4: scales of the next group
+
+  // W4: switch the accumulators to the units of the group whose scales are
+  // in s_nx (see cu above).
+  auto enter_group = [&]() {
+    if constexpr (KIND == GEMM_W4) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const float s = s_nx[j];
+      const bool use = (s != 0.f) && (cu[j] <= s * 0x1p64f);  // false for NaN
+      const float r = use ? cu[j] / s : 1.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) acc[i][j] *= r;
+      cu[j] = use ? s : cu[j];
+      mk[j] = use ? 0xF0F0F0F0u : 0u;
+      fix |= (!use && s != 0.f) ? (1 << j) : 0;
+    }
+    }
+  };
 
   auto mem_phase = [&](int ks) {
     const uint8_t* as = ring + (ks % NSTAGE) * STAGE;
@@ -230,12 +272,12 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
       }
     }
     if constexpr (KIND == GEMM_W4) {
-      if ((ks & 3) == 3) {  // last stage of a 256-group: fetch the group's scales for the fold
-        const int g = (ks0 + ks) >> 2;
+      if ((ks & 3) == 3 && ks + 1 < KS) {  // last stage of a 256-group: fetch the next group's scales
+        const int g = ((ks0 + ks) >> 2) + 1;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = min(n0 + wn0 + j * 16 + r16, N - 1);
-          s_grp[j] = sw[(int64_t)col * groups + g];
+          s_nx[j] = sw[(int64_t)col * groups + g];
         }
       }
     }
@@ -257,8 +299,8 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
       // interleave made the int4 kernel slower, which keeps the plain order).
       auto widen = [&](int j, bf16x8_t& b0, bf16x8_t& b1) {
         if constexpr (KIND == GEMM_W4) {
-          b0 = pp_widen_i4x8(fb[j].x);
-          b1 = pp_widen_i4x8(fb[j].y);
+          b0 = pp_widen_i4x8_x16(fb[j].x, mk[j]);
+          b1 = pp_widen_i4x8_x16(fb[j].y, mk[j]);
         } else {
           b0 = pp_widen_i8x8(fb[j].x, fb[j].y);
           b1 = pp_widen_i8x8(fb[j].z, fb[j].w);
@@ -294,15 +336,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
       }
     }
     if constexpr (KIND == GEMM_W4) {
-      if ((ks & 3) == 3) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            tot[i][j] += s_grp[j] * acc[i][j];
-            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
-      }
+      if ((ks & 3) == 3 && ks + 1 < KS) enter_group();
     }
   };
 
@@ -321,6 +355,14 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) ep_sa[i][r] = sa[min(m0 + wm0 + i * 16 + g4 * 4 + r, M - 1)];
+  }
+
+  if constexpr (KIND == GEMM_W4) {  // scales of the first group of the K range
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      cu[j] = 0.f;
+      s_nx[j] = sw[(int64_t)min(n0 + wn0 + j * 16 + r16, N - 1) * groups + (ks0 >> 2)];
+    }
   }
 
   // Stage ks+1 has landed once at most the loads of stages ks+2 .. ks+NSTAGE-1
@@ -344,6 +386,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
     __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(0));
   }
   barrier_only();
+  if constexpr (KIND == GEMM_W4) enter_group();
 
   // Both groups run the same body (memory phase, barrier, compute phase,
   // barrier); group 1 starts one barrier later and group 0 ends one barrier
@@ -365,6 +408,29 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   }
   if (grp == 0) barrier_only();
 
+  // W4 output of accumulator element (i, j, r): back from units of cu[j]
+  // (and from the 16x codes); a column with a skipped group is summed again
+  // exactly, group by group, straight from A and the codes (never taken for
+  // scales within 2^64 of each other along a row).
+  auto w4_value = [&](int i, int j, int r) -> float {
+    if (!((fix >> j) & 1)) return (acc[i][j][r] * 0.0625f) * cu[j];
+    const int row = m0 + wm0 + i * 16 + g4 * 4 + r, col = n0 + wn0 + j * 16 + r16;
+    const uint16_t* arow = reinterpret_cast<const uint16_t*>(A + (int64_t)row * lda_bytes);
+    const uint8_t* brow = B + (int64_t)col * ldb_bytes;
+    float total = 0.f;
+    for (int g = ks0 >> 2; g < (ks0 + KS) >> 2; ++g) {
+      const float sg = sw[(int64_t)col * groups + g];
+      if (sg == 0.f) continue;
+      float dot = 0.f;
+      for (int k = g * 256; k < g * 256 + 256; ++k) {
+        const int code = ((int)((uint32_t)brow[k >> 1] << ((k & 1) ? 24 : 28))) >> 28;
+        dot += __builtin_bit_cast(float, (uint32_t)arow[k] << 16) * (float)code;
+      }
+      total += sg * dot;
+    }
+    return total;
+  };
+
   if constexpr (PARTIAL) {
     // Raw sums of this K range, [split][m][n] with row pitch N.
     __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(0));
@@ -381,7 +447,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
           const int col = n0 + wn0 + j * 16 + r16;
           if (col >= N) continue;
           if constexpr (KIND == GEMM_W4)
-            pbase[(int64_t)row * N + col] = tot[i][j][r];
+            pbase[(int64_t)row * N + col] = w4_value(i, j, r);
           else
             pbase[(int64_t)row * N + col] = acc[i][j][r];
         }
@@ -400,7 +466,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
     } else if constexpr (KIND == GEMM_W8) {
       return acc[i][j][r] * ep_sw[j];
     } else {
-      return tot[i][j][r];
+      return w4_value(i, j, r);
     }
   };
   typedef typename std::conditional<OUT_BF16, __bf16, float>::type out_t;

@@ -289,6 +289,42 @@ def test_weight_only_ragged(kind, m, n, k):
     assert err < 1e-4
 
 
+@pytest.mark.parametrize("m,n,k", [(300, 600, 2048), (2048, 4096, 1024), (4000, 3000, 1024)])
+def test_w4_group_scale_edges(m, n, k):
+    """Hand-made int4 codes and group scales that the quantizer never emits,
+    one pattern per column class, on the split-K, 128x192 and 256x192 paths:
+    zero scales over nonzero codes (no contribution), scales 1e28 apart in
+    both orders, all-zero scales, and columns whose only nonzero codes sit in
+    the tiny-scale groups. Each class is compared on its own columns."""
+    d = dev()
+    announce("tp_qgemm_w4 group-scale edges", m, n, k)
+    rng = np.random.default_rng(m + n + k)
+    g = k // 256
+    codes = rng.integers(-7, 8, size=(n, k)).astype(np.int8)
+    s = (rng.uniform(0.5, 2.0, size=(n, g)) * 1e-2).astype(np.float32)
+    cls = np.arange(n) % 6
+    tiny = np.float32(1e-30)
+    s[cls == 1, 0] = 0.0                                   # zero scale over nonzero codes
+    s[cls == 2, 1::2] = tiny                               # normal, tiny, normal, ...
+    s[cls == 3, : g // 2] = tiny                           # tiny first, then normal
+    s[cls == 4] = 0.0                                      # every scale zero
+    s[cls == 5, 1::2] = tiny                               # codes only where the scale is tiny
+    c5 = codes[cls == 5].reshape(-1, g, 256)
+    c5[:, 0::2] = 0
+    codes[cls == 5] = c5.reshape(-1, k)
+    packed = oracle.pack_int4(codes)
+    x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    y = tp.tp_qgemm_w4(x.to(d), torch.from_numpy(packed).to(d), torch.from_numpy(s).to(d), rotate=False,
+                       out_dtype=torch.float32)
+    got = f64(y)
+    ref = oracle.qgemm_w4(f64(x), packed, s, rotate=False)
+    assert np.all(np.isfinite(got))
+    assert np.all(got[:, cls == 4] == 0.0)
+    for c in (0, 1, 2, 3, 5):
+        err = np.linalg.norm(got[:, cls == c] - ref[:, cls == c]) / np.linalg.norm(ref[:, cls == c])
+        assert err < 1e-5, f"column class {c}: relative error {err:.3e}"
+
+
 def test_w8_prerotated_padded_views():
     d = dev()
     announce("tp_qgemm_w8 pre-rotated bf16 A, padded A and C views")
