@@ -46,6 +46,9 @@ the design notes):
       codes rint(x'/sa) clamped to [-127, 127]; the int32 accumulator is the
       exact integer dot product; the output is acc * sa[m] * sw[n].
   R10 K must be a multiple of 256 (a group never straddles the end of a row).
+  R15 SwiGLU(g, u) = silu(g) * u, silu(x) = x / (1 + e^-x); its output h is
+      bf16, rounded once from the real value (oracle/ffn.py).
+  R16 h enters the down projection like any other activation.
 
 Parity pins live in tests/test_oracle.py; planted-fault controls in
 tests/test_controls.py.
@@ -63,6 +66,7 @@ from .quantize import (
     dequantize_int4,
 )
 from .products import qgemm_w8, qgemm_w4, qgemm_w8a8, int_accumulate
+from .ffn import silu_mul, swiglu_bf16, ffn_middle_int8, ffn_middle_rotated
 
 __all__ = [
     "GROUP",
@@ -76,6 +80,10 @@ __all__ = [
     "unpack_int4",
     "dequantize_int8",
     "dequantize_int4",
+    "silu_mul",
+    "swiglu_bf16",
+    "ffn_middle_int8",
+    "ffn_middle_rotated",
     "qgemm_w8",
     "qgemm_w4",
     "qgemm_w8a8",

@@ -315,3 +315,68 @@ def check_rotation_helps(quantize_weights_int8, dequantize_int8, rotate_groups, 
     plain = np.clip(np.rint(w / s0[:, None]), -127, 127) * s0[:, None]
     err_plain = np.linalg.norm(plain - w) / np.linalg.norm(w)
     assert err_rot < 0.5 * err_plain, (err_rot, err_plain)
+
+
+# ------------------------------------------------------------- FFN middle
+def check_swiglu(silu_mul, swiglu_bf16, seed=23):
+    """SwiGLU h = bf16(silu(g) * u), silu(x) = x / (1 + e^-x) (reading R15).
+
+    * closed forms: sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4, so
+      silu(ln 3) u = 3/4 ln 3 u and silu(-ln 3) u = -1/4 ln 3 u; silu(0) = 0;
+      for g >= 64, 1 + e^-g rounds to 1 in fp64 and silu(g) u = g u exactly;
+    * the identity silu(x) - silu(-x) = x on random x;
+    * bf16 values worked by hand: bf16(3/2 ln 3) = 211/128 and
+      bf16(-1/2 ln 3) = -141/256 (ln 3 = 1.0986...);
+    * rounding once, ties to even: with g = 64 and u = v / 64 (both exact),
+      h = bf16(v): v = 1 + 2^-8 (a tie) gives 1, v = 1 + 3 2^-8 (a tie) gives
+      1 + 2^-6, and v = 1 + 2^-8 + 2^-30 (just above the tie, within an fp32
+      half-ulp of it, so rounding through fp32 first would give 1) gives
+      1 + 2^-7.
+    """
+    ln3 = np.log(3.0)
+    for u in (1.0, -2.5, 7.0):
+        assert abs(silu_mul(ln3, u) - 0.75 * ln3 * u) <= 1e-15 * abs(ln3 * u), "silu(ln 3) != 3/4 ln 3"
+        assert abs(silu_mul(-ln3, u) + 0.25 * ln3 * u) <= 1e-15 * abs(ln3 * u), "silu(-ln 3) != -1/4 ln 3"
+        assert silu_mul(0.0, u) == 0.0
+        assert silu_mul(64.0, u) == 64.0 * u
+    x = np.random.default_rng(seed).uniform(-20, 20, size=1000)
+    d = silu_mul(x, 1.0) - silu_mul(-x, 1.0)
+    assert np.all(np.abs(d - x) <= 1e-14 * (1 + np.abs(x))), "silu(x) - silu(-x) != x"
+    assert swiglu_bf16(ln3, 2.0) == 211.0 / 128.0
+    assert swiglu_bf16(-ln3, 2.0) == -141.0 / 256.0
+    assert swiglu_bf16(64.0, (1 + 2.0 ** -8) / 64) == 1.0, "tie must round to even (down)"
+    assert swiglu_bf16(64.0, (1 + 3 * 2.0 ** -8) / 64) == 1 + 2.0 ** -6, "tie must round to even (up)"
+    assert swiglu_bf16(64.0, (1 + 2.0 ** -8 + 2.0 ** -30) / 64) == 1 + 2.0 ** -7, "rounded twice"
+    g = np.array([[ln3, -ln3], [64.0, 0.0]])
+    u = np.array([[2.0, 2.0], [(1 + 2.0 ** -8) / 64, 5.0]])
+    assert np.array_equal(swiglu_bf16(g, u), np.array([[211 / 128, -141 / 256], [1.0, 0.0]])), "elementwise"
+
+
+def check_ffn_middle(ffn_middle_int8, ffn_middle_rotated, quantize_activations_int8, bf16_round,
+                     hadamard_matrix, seed=24):
+    """The down projection's input from gate and up (reading R16).
+
+    Planted rows: xs with entries in {-1, 0, 1} and a 1 in every row; h = xs Q
+    per 256-group (multiples of 1/16 up to 16 in magnitude, so bf16-exact).
+    With g = 64 (silu(64) u = 64 u exactly) and u = h / 64, SwiGLU gives h
+    back, the rotation gives xs, the row maximum is 1, the scale is
+    fp32(1/127) and the codes are 127 xs. A random case must equal rotating
+    and quantizing bf16(silu(g) u) directly.
+    """
+    rng = np.random.default_rng(seed)
+    m, k = 4, 512
+    xs = rng.integers(-1, 2, size=(m, k)).astype(np.float64)
+    xs[:, 3] = 1.0
+    q = hadamard_matrix(256) / 16.0
+    h = np.concatenate([xs[:, j * 256:(j + 1) * 256] @ q for j in range(k // 256)], axis=1)
+    assert np.array_equal(bf16_round(h), h), "planted rows must be bf16-exact"
+    g = np.full((m, k), 64.0)
+    qa, sa = ffn_middle_int8(g, h / 64.0)
+    assert np.all(sa == np.float32(1.0 / 127.0)), "scale of a row whose rotated maximum is 1"
+    assert np.array_equal(qa, (127 * xs).astype(np.int8)), "codes of the planted rows"
+    assert np.array_equal(ffn_middle_rotated(g, h / 64.0), xs), "rotated planted rows"
+    gg = rng.standard_normal((3, 768))
+    uu = rng.standard_normal((3, 768))
+    q1, s1 = ffn_middle_int8(gg, uu)
+    q2, s2 = quantize_activations_int8(bf16_round(gg * uu / (1 + np.exp(-gg))), rotate=True)
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2), "not the quantized rotation of bf16(silu(g) u)"

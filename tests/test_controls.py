@@ -128,3 +128,52 @@ def test_w8a8_unrotated_activations_caught():
         return oracle.qgemm_w8a8(x, q, sw, rotate=False)
     with pytest.raises(AssertionError):
         pins.check_planted_w8a8(w8a8_no_rot, oracle.hadamard_matrix)
+
+
+# ------------------------------------------------------------ FFN middle
+def _silu_mul_sigmoid_only(g, u):  # forgets the factor g
+    g = np.asarray(g, dtype=np.float64)
+    return np.asarray(u, dtype=np.float64) / (1.0 + np.exp(-g))
+
+
+def _silu_mul_swapped(g, u):  # silu(u) * g
+    return oracle.silu_mul(u, g)
+
+
+def _silu_mul_sign(g, u):  # e^+g in the denominator
+    g = np.asarray(g, dtype=np.float64)
+    return g * np.asarray(u, dtype=np.float64) / (1.0 + np.exp(g))
+
+
+@pytest.mark.parametrize("bad", [_silu_mul_sigmoid_only, _silu_mul_swapped, _silu_mul_sign])
+def test_swiglu_formula_faults_caught(bad):
+    with pytest.raises(AssertionError):
+        pins.check_swiglu(bad, lambda g, u: oracle.bf16_round(bad(g, u)))
+
+
+def test_swiglu_double_rounding_caught():
+    def through_fp32(g, u):
+        return oracle.bf16_round(np.asarray(oracle.silu_mul(g, u), dtype=np.float32).astype(np.float64))
+    with pytest.raises(AssertionError):
+        pins.check_swiglu(oracle.silu_mul, through_fp32)
+
+
+def test_swiglu_missing_rounding_caught():
+    with pytest.raises(AssertionError):
+        pins.check_swiglu(oracle.silu_mul, oracle.silu_mul)
+
+
+def test_ffn_middle_without_rotation_caught():
+    def no_rot(g, u):
+        return oracle.quantize_activations_int8(oracle.swiglu_bf16(g, u), rotate=False)
+    with pytest.raises(AssertionError):
+        pins.check_ffn_middle(no_rot, oracle.ffn_middle_rotated, oracle.quantize_activations_int8,
+                              oracle.bf16_round, oracle.hadamard_matrix)
+
+
+def test_ffn_middle_unrounded_caught():
+    def unrounded(g, u):
+        return oracle.quantize_activations_int8(oracle.silu_mul(g, u), rotate=True)
+    with pytest.raises(AssertionError):
+        pins.check_ffn_middle(unrounded, oracle.ffn_middle_rotated, oracle.quantize_activations_int8,
+                              oracle.bf16_round, oracle.hadamard_matrix)

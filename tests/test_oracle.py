@@ -73,3 +73,12 @@ def test_activation_quant_zero_row():
 def test_refuses_ragged_k():
     with pytest.raises(ValueError):
         oracle.rotate_groups(np.zeros((1, 300)))
+
+
+def test_swiglu():
+    pins.check_swiglu(oracle.silu_mul, oracle.swiglu_bf16)
+
+
+def test_ffn_middle():
+    pins.check_ffn_middle(oracle.ffn_middle_int8, oracle.ffn_middle_rotated, oracle.quantize_activations_int8,
+                          oracle.bf16_round, oracle.hadamard_matrix)

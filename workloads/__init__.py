@@ -20,6 +20,12 @@ describe: 256 latent + 32 prompt rows at a 256x256 image, 4096 latent rows at
   dit_qkv / dit_out / dit_gateup / dit_down   M=4096; 3072->9216, 3072->3072,
                                        3072->24576, 12288->3072; as proj256
 
+FFN middle (gate and up of a SwiGLU feed-forward, G then U ~ N(0,1), fp32):
+  ffn_mid_w8a8  M=4096, K=12288, seed 404: the fp32 gate+up output of the
+                W8A8 block, turned into the int8 input of dit_down
+  ffn_mid_w4    M=4032, K=12288, seed 3: ffn_down's G and U (same draws),
+                turned into its rotated bf16 input
+
 Recipe: numpy default_rng(seed) (PCG64). Draw order: activations (G then U for
 ffn_down), weights, activation outlier columns, weight outlier columns (each a
 choice without replacement). Outlier count is round(0.005*K) unless fixed.
@@ -123,3 +129,35 @@ def random_rows(shape, seed, dtype="f32", scale=1.0):
     rng = np.random.default_rng(seed)
     a = rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)
     return _to_dtype(a, dtype)
+
+
+@dataclass(frozen=True)
+class FfnMiddle:
+    name: str
+    m: int
+    k: int
+    seed: int
+    in_dtype: str   # "f32" or "bf16"
+    out: str        # "i8" or "bf16"
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+FFN_MID_W8A8 = FfnMiddle("ffn_mid_w8a8", 4096, 12288, 404, "f32", "i8")
+FFN_MID_W4 = FfnMiddle("ffn_mid_w4", 4032, 12288, 3, "f32", "bf16")
+
+
+def gate_up(w: FfnMiddle, rows=None, fused=False):
+    """Gate and up activations [M, K] (G drawn first, then U, both N(0,1) in
+    fp32, rounded to bf16 if in_dtype says so). fused=True returns one
+    [M, 2K] tensor holding G in columns [0, K) and U in [K, 2K), the layout a
+    gate+up projection writes; otherwise (G, U)."""
+    rng = np.random.default_rng(w.seed)
+    g = rng.standard_normal((w.m, w.k), dtype=np.float32)
+    u = rng.standard_normal((w.m, w.k), dtype=np.float32)
+    if rows is not None:
+        g, u = g[:rows], u[:rows]
+    if fused:
+        return _to_dtype(np.concatenate([g, u], axis=1), w.in_dtype)
+    return _to_dtype(g, w.in_dtype), _to_dtype(u, w.in_dtype)
