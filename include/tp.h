@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 2
+#define TP_ABI_VERSION 3
 
 typedef enum tp_status {
   TP_OK = 0,
@@ -145,6 +145,37 @@ tp_status tp_quantize_rows_int8(const void* x, tp_dtype x_dtype, int64_t m, int6
                                 int64_t ldx, int a_flags, int8_t* qa, int64_t ldqa, float* sa,
                                 hipStream_t stream);
 
+/* out_kind of tp_swiglu_rotate. */
+#define TP_FFN_OUT_I8 0   /* int8 codes [m, k] and fp32 scales [m] */
+#define TP_FFN_OUT_BF16 1 /* rotated bf16 rows [m, k]              */
+
+/*
+ * tp_swiglu_rotate -- the input of an FFN's down projection, fused: the
+ * SwiGLU hidden activation h = bf16(silu(gate) * up), silu(x) = x / (1 + e^-x),
+ * is rotated per 256-group and written as per-row int8 codes or as rotated
+ * bf16 rows, without h ever being stored (tensai docs, "画像生成", section
+ * "何が走るか": every block is attention plus a SwiGLU feed-forward; section
+ * "幅とメモリ": the product's input is rotated per 256 columns on the device;
+ * TensorFold pull request #948: bf16 activations, and the row kernels around
+ * the projections as the candidates for fusion).
+ *
+ *   gate, up  [m, k], both in_dtype (TP_F32 or TP_BF16), row pitches ld_gate
+ *             and ld_up (elements). They may be the two column halves of one
+ *             [m, 2k] gate+up output, and may overlap each other.
+ *   h[r, j]   the real value silu(gate[r, j]) * up[r, j] rounded once to bf16
+ *             (nearest even); fp32 shortcuts are taken only where they provably
+ *             round the same way.
+ *   out_kind  TP_FFN_OUT_I8: y int8 [m, k], row pitch ldy bytes, and scales
+ *             fp32 [m]: bit-identical to tp_quantize_rows_int8 of h with
+ *             TP_A_ROTATE. TP_FFN_OUT_BF16: y bf16 [m, k], row pitch ldy
+ *             elements: identical to tp_hadamard_rotate_rows of h to TP_BF16;
+ *             scales is not used and may be NULL.
+ *   y and scales must not overlap gate, up or each other.
+ */
+tp_status tp_swiglu_rotate(const void* gate, int64_t ld_gate, const void* up, int64_t ld_up,
+                           tp_dtype in_dtype, int64_t m, int64_t k, int out_kind, void* y,
+                           int64_t ldy, float* scales, hipStream_t stream);
+
 /*
  * tp_workspace_size -- bytes of device workspace the product `op` needs for
  * these sizes and a_flags (0 when none is needed). Returns 0 for invalid
@@ -153,8 +184,9 @@ tp_status tp_quantize_rows_int8(const void* x, tp_dtype x_dtype, int64_t m, int6
  * The workspace holds, in this order: the rotated bf16 activations (W8, W4
  * with TP_A_ROTATE: 2 m k bytes) or the activation codes and scales (W8A8
  * unless the caller takes them through qa_out / sa_out); then, for products
- * with few rows (m <= 64), the split-K partial sums (4 m n bytes per split;
- * the split count depends on m, n and k). The size therefore depends on all
+ * whose output tiles would leave compute units idle (few rows, or a small
+ * output), the split-K partial sums (4 m n bytes per split; the split count
+ * depends on m, n and k). The size therefore depends on all
  * of op, m, n, k and a_flags. A product given less than it needs returns
  * TP_ERR_WORKSPACE_TOO_SMALL; W8A8 with both qa_out and sa_out needs only the
  * partial-sum part. The contents are scratch: nothing is kept between calls.

@@ -19,7 +19,7 @@ of the computation runs in the library's HIP kernels; there is no CPU path.
 import torch
 
 from . import _lib
-from ._lib import TPError, TP_A_PREROTATED, TP_A_ROTATE  # noqa: F401
+from ._lib import TPError, TP_A_PREROTATED, TP_A_ROTATE, TP_FFN_OUT_BF16, TP_FFN_OUT_I8  # noqa: F401
 
 _DTYPE = {torch.float32: _lib.TP_F32, torch.bfloat16: _lib.TP_BF16}
 
@@ -107,6 +107,32 @@ def tp_quantize_rows_int8(x, rotate=True, qa=None, sa=None, stream=None):
     _lib.check(_lib.load().tp_quantize_rows_int8(x.data_ptr(), _dt(x), m, k, ldx, flags, qa.data_ptr(), ldqa,
                                                  sa.data_ptr(), _stream(stream)))
     return qa, sa
+
+
+def tp_swiglu_rotate(gate, up, out_kind="i8", out=None, scales=None, stream=None):
+    """h = bf16(silu(gate) * up) rotated per 256-group, as int8 codes with one
+    fp32 scale per row (out_kind "i8": returns (codes, scales)) or as rotated
+    bf16 rows (out_kind "bf16": returns the rows). gate and up: [m, k], both
+    fp32 or both bf16 (may be column views of one gate+up output)."""
+    if out_kind not in ("i8", "bf16"):
+        raise ValueError("out_kind must be 'i8' or 'bf16'")
+    if gate.shape != up.shape or gate.dtype != up.dtype:
+        raise ValueError("gate and up must have the same shape and dtype")
+    ldg = _mat(gate, "gate")
+    ldu = _mat(up, "up")
+    m, k = gate.shape
+    i8 = out_kind == "i8"
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.int8 if i8 else torch.bfloat16, device=gate.device)
+    ldy = _mat(out, "out")
+    if i8:
+        if scales is None:
+            scales = torch.empty((m,), dtype=torch.float32, device=gate.device)
+        _vec(scales, "scales", m)
+    _lib.check(_lib.load().tp_swiglu_rotate(gate.data_ptr(), ldg, up.data_ptr(), ldu, _dt(gate), m, k,
+                                            TP_FFN_OUT_I8 if i8 else TP_FFN_OUT_BF16, out.data_ptr(), ldy,
+                                            scales.data_ptr() if i8 else None, _stream(stream)))
+    return (out, scales) if i8 else out
 
 
 def _workspace(op, m, n, k, flags, device, workspace):

@@ -29,6 +29,7 @@ STATUS_NAMES = {
 TP_F32, TP_BF16 = 0, 1
 TP_A_PREROTATED, TP_A_ROTATE = 0, 1
 TP_OP_QGEMM_W8, TP_OP_QGEMM_W4, TP_OP_QGEMM_W8A8, TP_OP_QGEMM_W8A8_PREQUANTIZED = 1, 2, 3, 4
+TP_FFN_OUT_I8, TP_FFN_OUT_BF16 = 0, 1
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -40,6 +41,7 @@ SIGNATURES = {
     "tp_rotate_quantize_weights": (_int, [_p, _int, _i64, _i64, _i64, _int, _p, _i64, _p, _p]),
     "tp_hadamard_rotate_rows": (_int, [_p, _int, _i64, _i64, _i64, _p, _int, _i64, _p]),
     "tp_quantize_rows_int8": (_int, [_p, _int, _i64, _i64, _i64, _int, _p, _i64, _p, _p]),
+    "tp_swiglu_rotate": (_int, [_p, _i64, _p, _i64, _int, _i64, _i64, _int, _p, _i64, _p, _p]),
     "tp_workspace_size": (_sz, [_int, _i64, _i64, _i64, _int]),
     "tp_qgemm_w8": (_int, [_p, _int, _i64, _int, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _sz, _p]),
     "tp_qgemm_w4": (_int, [_p, _int, _i64, _int, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _sz, _p]),

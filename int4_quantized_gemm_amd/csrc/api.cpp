@@ -260,6 +260,30 @@ tp_status tp_quantize_rows_int8(const void* x, tp_dtype x_dtype, int64_t m, int6
                     "activation quantize launch");
 }
 
+tp_status tp_swiglu_rotate(const void* gate, int64_t ld_gate, const void* up, int64_t ld_up, tp_dtype in_dtype,
+                           int64_t m, int64_t k, int out_kind, void* y, int64_t ldy, float* scales,
+                           hipStream_t stream) {
+  if (!dtype_ok(in_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "in_dtype %d is not TP_F32 or TP_BF16", (int)in_dtype);
+  if (out_kind != TP_FFN_OUT_I8 && out_kind != TP_FFN_OUT_BF16) return fail(TP_ERR_BAD_FLAGS, "out_kind=%d", out_kind);
+  TP_TRY(check_sizes(m, 0, k));
+  const bool i8 = out_kind == TP_FFN_OUT_I8;
+  const int64_t es = dtype_size(in_dtype), ys = i8 ? 1 : 2;
+  Extent eg, eu, ey, esc;
+  TP_TRY(check_matrix("gate", gate, m, k * es, ld_gate, es, &eg));
+  TP_TRY(check_matrix("up", up, m, k * es, ld_up, es, &eu));
+  TP_TRY(check_matrix("y", y, m, k * ys, ldy, ys, &ey));
+  if (i8) {
+    TP_TRY(check_vector("scales", scales, m, &esc));
+    if (overlaps(esc, eg) || overlaps(esc, eu) || overlaps(esc, ey))
+      return fail(TP_ERR_BAD_ALIASING, "scales must not overlap gate, up or y");
+  }
+  if (overlaps(ey, eg) || overlaps(ey, eu)) return fail(TP_ERR_BAD_ALIASING, "y must not overlap gate or up");
+  if (m == 0) return ok();
+  return hip_status(tp::launch_swiglu_rotate(gate, ld_gate, up, ld_up, in_dtype == TP_BF16, m, k, i8, y, ldy,
+                                             i8 ? scales : nullptr, stream),
+                    "swiglu rotate launch");
+}
+
 namespace {
 
 // Shared by the two weight-only products.

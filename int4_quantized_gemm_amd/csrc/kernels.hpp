@@ -16,6 +16,11 @@ hipError_t launch_rotate_rows(const void* x, bool x_bf16, int64_t ldx, void* y, 
 hipError_t launch_rotq_rows(const void* x, bool x_bf16, int64_t ldx, int64_t rows, int64_t k, bool rotate,
                             int bits, void* q, int64_t ldq, float* scales, hipStream_t stream);
 
+// FFN middle: h = bf16(silu(g) * u), rotated per 256-group, then int8 codes
+// with one scale per row (out_i8) or bf16 rows (scales unused).
+hipError_t launch_swiglu_rotate(const void* g, int64_t ldg, const void* u, int64_t ldu, bool in_bf16, int64_t m,
+                                int64_t k, bool out_i8, void* y, int64_t ldy, float* scales, hipStream_t stream);
+
 enum GemmKind { GEMM_W8 = 0, GEMM_W4 = 1, GEMM_W8A8 = 2 };
 
 struct GemmArgs {

@@ -9,6 +9,13 @@
 //  * k_rotq_rows<I4_GRP> rotate in fp64, then int4 with one scale per
 //                        (row, 256-group), packed two per byte (the "-q4" width
 //                        of section "幅とメモリ").
+//  * k_rotq_i8_fast      the int8 rows of k_rotq_rows<I8_ROW> in fp32 with an
+//                        exact fallback.
+//
+// Every kernel reads its rows through a source (RowSrc: a buffer; SwigluSrc:
+// the FFN middle h = bf16(silu(g) * u) of a gate and an up buffer, computed on
+// the fly, so that the down projection's input is rotated and quantized
+// without a round trip through memory).
 //
 // Work layout: a 256-group is held by 32 lanes (a half wave), 8 consecutive
 // elements per lane, so every global access is a 16- or 32-byte vector per
@@ -22,9 +29,8 @@ namespace tp {
 
 // ---------------------------------------------------------------- rotate rows
 // One (row, group) unit per half wave; 4 waves = 8 units per block.
-template <typename TIn, typename TOut>
-__global__ __launch_bounds__(256) void k_rotate_rows(const TIn* x, int64_t ldx, TOut* y, int64_t ldy,
-                                                     int64_t units, int groups) {
+template <typename Src, typename TOut>
+__global__ __launch_bounds__(256) void k_rotate_rows(Src src, TOut* y, int64_t ldy, int64_t units, int groups) {
   const int lane = threadIdx.x & 63;
   const int lane32 = lane & 31;
   const int64_t unit = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
@@ -32,7 +38,7 @@ __global__ __launch_bounds__(256) void k_rotate_rows(const TIn* x, int64_t ldx, 
   const int64_t row = unit / groups;
   const int64_t col = (unit - row * groups) * 256 + lane32 * 8;
   float v[8];
-  load8(x + row * ldx + col, v);
+  src.load8(row, col, v);
   fwht256_lane8(v, lane32);
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] *= 0.0625f;
@@ -42,9 +48,10 @@ __global__ __launch_bounds__(256) void k_rotate_rows(const TIn* x, int64_t ldx, 
 // ------------------------------------------------------- rotate and quantize
 enum { MODE_I8_ROW = 0, MODE_I4_GROUP = 1 };
 
-template <typename TIn>
-__device__ __forceinline__ void load_group(const TIn* p, bool rotate, int lane32, double (&v)[8]) {
-  load8d(p, v);
+template <typename Src>
+__device__ __forceinline__ void load_group(const Src& src, int64_t row, int64_t col, bool rotate, int lane32,
+                                           double (&v)[8]) {
+  src.load8d(row, col, v);
   if (rotate) {
     fwht256_lane8(v, lane32);
 #pragma unroll
@@ -53,22 +60,22 @@ __device__ __forceinline__ void load_group(const TIn* p, bool rotate, int lane32
 }
 
 // One wave per row. Half wave h of the wave processes groups h, h+2, h+4, ...
-template <typename TIn, int MODE>
-__global__ __launch_bounds__(256) void k_rotq_rows(const TIn* x, int64_t ldx, int64_t rows, int groups,
-                                                   int rotate, uint8_t* q, int64_t ldq, float* scales) {
+template <typename Src, int MODE>
+__global__ __launch_bounds__(256) void k_rotq_rows(Src src, int64_t rows, int groups, int rotate, uint8_t* q,
+                                                   int64_t ldq, float* scales) {
   const int lane = threadIdx.x & 63;
   const int lane32 = lane & 31;
   const int half = lane >> 5;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;  // uniform over the wave
-  const TIn* src = x + row * ldx + lane32 * 8;
+  const int64_t col0 = lane32 * 8;
   uint8_t* dst = q + row * ldq;
 
   if (MODE == MODE_I8_ROW) {
     double amax = 0.0;
     for (int g = half; g < groups; g += 2) {
       double v[8];
-      load_group(src + (int64_t)g * 256, rotate != 0, lane32, v);
+      load_group(src, row, col0 + (int64_t)g * 256, rotate != 0, lane32, v);
 #pragma unroll
       for (int j = 0; j < 8; ++j) amax = fmax(amax, fabs(v[j]));
     }
@@ -78,7 +85,7 @@ __global__ __launch_bounds__(256) void k_rotq_rows(const TIn* x, int64_t ldx, in
     const double inv = s > 0.0f ? 1.0 / s64 : 0.0;
     for (int g = half; g < groups; g += 2) {
       double v[8];
-      load_group(src + (int64_t)g * 256, rotate != 0, lane32, v);
+      load_group(src, row, col0 + (int64_t)g * 256, rotate != 0, lane32, v);
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(256) void k_rotq_rows(const TIn* x, int64_t ldx, in
   } else {
     for (int g = half; g < groups; g += 2) {
       double v[8];
-      load_group(src + (int64_t)g * 256, rotate != 0, lane32, v);
+      load_group(src, row, col0 + (int64_t)g * 256, rotate != 0, lane32, v);
       double amax = 0.0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) amax = fmax(amax, fabs(v[j]));
@@ -241,6 +248,96 @@ struct Raw16<float> {
   __device__ __forceinline__ float get(int i) const { return w[i]; }
 };
 
+// ------------------------------------------------------------- input sources
+// A source yields 8 or 16 consecutive elements of a row: as fp32 (load8), as
+// fp64 (load8d), or as the raw words the fast int8 kernel keeps for its exact
+// fallbacks (load16, into Raw16<raw_elem>).
+
+// Rows of a [rows, k] buffer of fp32 or bf16 (uint16_t) elements.
+template <typename T>
+struct RowSrc {
+  typedef T raw_elem;
+  const T* x;
+  int64_t ldx;
+  __device__ __forceinline__ void load8(int64_t r, int64_t c, float (&v)[8]) const { tp::load8(x + r * ldx + c, v); }
+  __device__ __forceinline__ void load8d(int64_t r, int64_t c, double (&v)[8]) const {
+    tp::load8d(x + r * ldx + c, v);
+  }
+  __device__ __forceinline__ void load16(int64_t r, int64_t c, Raw16<T>& raw) const { raw.load(x + r * ldx + c); }
+};
+
+// bf16 bits of silu(g) * u = g u / (1 + e^-g), rounded once (to nearest even)
+// from the real value: the SwiGLU feed-forward's hidden activation, a bf16
+// tensor (tensai docs, "画像生成", section "何が走るか": every block is
+// attention plus a SwiGLU feed-forward; TensorFold pull request #948: bf16
+// activations rounded where the reference rounds them).
+//
+// fp32 first: e = v_exp_f32(-g log2 e), h = (g u) v_rcp_f32(1 + e). Relative
+// error, to first order: |g| 2^-24 from the rounded exponent argument and
+// |g| 2^-25 from the rounded log2 e, 2^-23 each from v_exp_f32 and v_rcp_f32,
+// 2^-24 each from 1 + e, g u and the last product: below (|g| + 8) 2^-24. With
+// h in [2^E, 2^(E+1)) the real value is then within (|g| + 8) fp32 ulps of h,
+// and rounding to bf16 depends only on where the low 16 bits of h sit against
+// the midpoint 0x8000; when they are farther than 4 (|g| + 8) + 8 ulps from it
+// (a 4x margin), h rounds like the real value. Otherwise, and for |g| > 64,
+// |h| < 2^-100 or non-finite h, the value is recomputed in fp64 and rounded
+// to bf16 through fp32 with round-to-odd (no double rounding).
+__device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+  const float h = (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
+  const uint32_t b = __builtin_bit_cast(uint32_t, h);
+  const float ag = fabsf(g), ah = fabsf(h);
+  const float dist = fabsf((float)((int)(b & 0xFFFFu) - 0x8000));
+  if (ag <= 64.f && ah >= 0x1p-100f && ah < 0x1p127f && dist > 4.f * (ag + 8.f) + 8.f)
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  const double hd = ((double)g * (double)u) / (1.0 + exp(-(double)g));
+  if (hd != hd) return 0x7FC0u;
+  const float f = __double2float_rz(hd);
+  uint32_t fb = __builtin_bit_cast(uint32_t, f);
+  if ((double)f != hd) fb |= 1u;
+  return (fb + 0x7FFFu + ((fb >> 16) & 1u)) >> 16;
+}
+
+// h = bf16(silu(g) * u) of a gate and an up buffer ([rows, k], both fp32 or
+// both bf16), element by element.
+template <typename T>
+struct SwigluSrc {
+  typedef uint16_t raw_elem;
+  const T* g;
+  int64_t ldg;
+  const T* u;
+  int64_t ldu;
+  __device__ __forceinline__ void bits8(int64_t r, int64_t c, uint32_t (&hb)[8]) const {
+    float gv[8], uv[8];
+    tp::load8(g + r * ldg + c, gv);
+    tp::load8(u + r * ldu + c, uv);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hb[j] = swiglu_bf16(gv[j], uv[j]);
+  }
+  __device__ __forceinline__ void load8(int64_t r, int64_t c, float (&v)[8]) const {
+    uint32_t hb[8];
+    bits8(r, c, hb);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_bit_cast(float, hb[j] << 16);
+  }
+  __device__ __forceinline__ void load8d(int64_t r, int64_t c, double (&v)[8]) const {
+    float f[8];
+    load8(r, c, f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (double)f[j];
+  }
+  __device__ __forceinline__ void load16(int64_t r, int64_t c, Raw16<uint16_t>& raw) const {
+    uint32_t lo[8], hi[8];
+    bits8(r, c, lo);
+    bits8(r, c + 8, hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      raw.w[i] = lo[2 * i] | (lo[2 * i + 1] << 16);
+      raw.w[4 + i] = hi[2 * i] | (hi[2 * i + 1] << 16);
+    }
+  }
+};
+
 template <int M>
 __device__ __forceinline__ double xor16d(double v) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
@@ -285,10 +382,11 @@ constexpr float RQ_MAGIC = 12582912.0f;  // 1.5 * 2^23: adding it rounds to an i
 // WPR = 4: one block per row, the four waves split the groups (k <= 48 * 256).
 // Three waves per SIMD: the register budget (166) that keeps every input in
 // registers for the exact fallbacks without spilling.
-template <typename TIn, int WPR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_rotq_i8_fast(const TIn* __restrict__ x, int64_t ldx, int64_t rows,
+template <typename Src, int WPR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_rotq_i8_fast(Src src, int64_t rows,
                                                       int groups, int rotate, int8_t* __restrict__ q, int64_t ldq,
                                                       float* __restrict__ scales) {
+  typedef typename Src::raw_elem TIn;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int set = lane >> 4, l16 = lane & 15;
   __shared__ __align__(16) uint8_t lds[16 * RQ_ROW_BYTES];
@@ -309,7 +407,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     gb = min(groups, wave * gpw);
     ge = min(groups, gb + gpw);
   }
-  const TIn* xr = x + row * ldx;
 
   // Load every group of this wave (up to 3 per 16-lane row) and transform it.
   Raw16<TIn> raw[3];
@@ -320,7 +417,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   for (int u = 0; u < 3; ++u) {
     has[u] = gb + set + 4 * u < ge;
     if (has[u])
-      raw[u].load(xr + (int64_t)(gb + set + 4 * u) * 256 + l16 * 16);
+      src.load16(row, (int64_t)(gb + set + 4 * u) * 256 + l16 * 16, raw[u]);
     else
       raw[u].zero();
   }
@@ -454,66 +551,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 }
 
 // ------------------------------------------------------------------ launchers
-hipError_t launch_rotate_rows(const void* x, bool x_bf16, int64_t ldx, void* y, bool y_bf16, int64_t ldy,
-                              int64_t m, int64_t k, hipStream_t stream) {
+template <typename Src, typename TOut>
+static hipError_t rotate_from(const Src& src, TOut* y, int64_t ldy, int64_t m, int64_t k, hipStream_t stream) {
   const int groups = (int)(k / 256);
   const int64_t units = m * groups;
   const dim3 grid((unsigned)((units + 7) / 8)), block(256);
-  if (x_bf16 && y_bf16)
-    hipLaunchKernelGGL((k_rotate_rows<uint16_t, uint16_t>), grid, block, 0, stream, (const uint16_t*)x, ldx,
-                       (uint16_t*)y, ldy, units, groups);
-  else if (x_bf16)
-    hipLaunchKernelGGL((k_rotate_rows<uint16_t, float>), grid, block, 0, stream, (const uint16_t*)x, ldx,
-                       (float*)y, ldy, units, groups);
-  else if (y_bf16)
-    hipLaunchKernelGGL((k_rotate_rows<float, uint16_t>), grid, block, 0, stream, (const float*)x, ldx,
-                       (uint16_t*)y, ldy, units, groups);
-  else
-    hipLaunchKernelGGL((k_rotate_rows<float, float>), grid, block, 0, stream, (const float*)x, ldx,
-                       (float*)y, ldy, units, groups);
+  hipLaunchKernelGGL((k_rotate_rows<Src, TOut>), grid, block, 0, stream, src, y, ldy, units, groups);
   return hipGetLastError();
+}
+
+// int8 rows: the fast kernel up to 48 groups, the fp64 one above.
+template <typename Src>
+static hipError_t rotq_i8_from(const Src& src, int64_t rows, int groups, int rot, int8_t* q8, int64_t ldq,
+                               float* scales, hipStream_t stream) {
+  const dim3 block(256);
+  if (groups <= 12)
+    hipLaunchKernelGGL((k_rotq_i8_fast<Src, 1>), dim3((unsigned)((rows + 3) / 4)), block, 0, stream, src, rows,
+                       groups, rot, q8, ldq, scales);
+  else if (groups <= 48)
+    hipLaunchKernelGGL((k_rotq_i8_fast<Src, 4>), dim3((unsigned)rows), block, 0, stream, src, rows, groups, rot, q8,
+                       ldq, scales);
+  else
+    hipLaunchKernelGGL((k_rotq_rows<Src, MODE_I8_ROW>), dim3((unsigned)((rows + 3) / 4)), block, 0, stream, src,
+                       rows, groups, rot, (uint8_t*)q8, ldq, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate_rows(const void* x, bool x_bf16, int64_t ldx, void* y, bool y_bf16, int64_t ldy,
+                              int64_t m, int64_t k, hipStream_t stream) {
+  if (x_bf16) {
+    const RowSrc<uint16_t> src{(const uint16_t*)x, ldx};
+    return y_bf16 ? rotate_from(src, (uint16_t*)y, ldy, m, k, stream) : rotate_from(src, (float*)y, ldy, m, k, stream);
+  }
+  const RowSrc<float> src{(const float*)x, ldx};
+  return y_bf16 ? rotate_from(src, (uint16_t*)y, ldy, m, k, stream) : rotate_from(src, (float*)y, ldy, m, k, stream);
 }
 
 hipError_t launch_rotq_rows(const void* x, bool x_bf16, int64_t ldx, int64_t rows, int64_t k, bool rotate,
                             int bits, void* q, int64_t ldq, float* scales, hipStream_t stream) {
   const int groups = (int)(k / 256);
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-  uint8_t* qb = (uint8_t*)q;
   const int rot = rotate ? 1 : 0;
-  if (bits == 8 && groups <= 48) {
-    int8_t* q8 = (int8_t*)q;
-    if (groups <= 12) {
-      if (x_bf16)
-        hipLaunchKernelGGL((k_rotq_i8_fast<uint16_t, 1>), grid, block, 0, stream, (const uint16_t*)x, ldx, rows,
-                           groups, rot, q8, ldq, scales);
-      else
-        hipLaunchKernelGGL((k_rotq_i8_fast<float, 1>), grid, block, 0, stream, (const float*)x, ldx, rows, groups,
-                           rot, q8, ldq, scales);
-    } else {
-      const dim3 grid_rows((unsigned)rows);
-      if (x_bf16)
-        hipLaunchKernelGGL((k_rotq_i8_fast<uint16_t, 4>), grid_rows, block, 0, stream, (const uint16_t*)x, ldx,
-                           rows, groups, rot, q8, ldq, scales);
-      else
-        hipLaunchKernelGGL((k_rotq_i8_fast<float, 4>), grid_rows, block, 0, stream, (const float*)x, ldx, rows,
-                           groups, rot, q8, ldq, scales);
-    }
-  } else if (bits == 8) {
-    if (x_bf16)
-      hipLaunchKernelGGL((k_rotq_rows<uint16_t, MODE_I8_ROW>), grid, block, 0, stream, (const uint16_t*)x, ldx,
-                         rows, groups, rot, qb, ldq, scales);
-    else
-      hipLaunchKernelGGL((k_rotq_rows<float, MODE_I8_ROW>), grid, block, 0, stream, (const float*)x, ldx, rows,
-                         groups, rot, qb, ldq, scales);
-  } else {
-    if (x_bf16)
-      hipLaunchKernelGGL((k_rotq_rows<uint16_t, MODE_I4_GROUP>), grid, block, 0, stream, (const uint16_t*)x,
-                         ldx, rows, groups, rot, qb, ldq, scales);
-    else
-      hipLaunchKernelGGL((k_rotq_rows<float, MODE_I4_GROUP>), grid, block, 0, stream, (const float*)x, ldx,
-                         rows, groups, rot, qb, ldq, scales);
+  if (bits == 8) {
+    if (x_bf16) return rotq_i8_from(RowSrc<uint16_t>{(const uint16_t*)x, ldx}, rows, groups, rot, (int8_t*)q, ldq,
+                                    scales, stream);
+    return rotq_i8_from(RowSrc<float>{(const float*)x, ldx}, rows, groups, rot, (int8_t*)q, ldq, scales, stream);
   }
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (x_bf16)
+    hipLaunchKernelGGL((k_rotq_rows<RowSrc<uint16_t>, MODE_I4_GROUP>), grid, block, 0, stream,
+                       RowSrc<uint16_t>{(const uint16_t*)x, ldx}, rows, groups, rot, (uint8_t*)q, ldq, scales);
+  else
+    hipLaunchKernelGGL((k_rotq_rows<RowSrc<float>, MODE_I4_GROUP>), grid, block, 0, stream,
+                       RowSrc<float>{(const float*)x, ldx}, rows, groups, rot, (uint8_t*)q, ldq, scales);
   return hipGetLastError();
+}
+
+hipError_t launch_swiglu_rotate(const void* g, int64_t ldg, const void* u, int64_t ldu, bool in_bf16, int64_t m,
+                                int64_t k, bool out_i8, void* y, int64_t ldy, float* scales, hipStream_t stream) {
+  const int groups = (int)(k / 256);
+  if (in_bf16) {
+    const SwigluSrc<uint16_t> src{(const uint16_t*)g, ldg, (const uint16_t*)u, ldu};
+    if (out_i8) return rotq_i8_from(src, m, groups, 1, (int8_t*)y, ldy, scales, stream);
+    return rotate_from(src, (uint16_t*)y, ldy, m, k, stream);
+  }
+  const SwigluSrc<float> src{(const float*)g, ldg, (const float*)u, ldu};
+  if (out_i8) return rotq_i8_from(src, m, groups, 1, (int8_t*)y, ldy, scales, stream);
+  return rotate_from(src, (uint16_t*)y, ldy, m, k, stream);
 }
 
 }  // namespace tp

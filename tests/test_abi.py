@@ -41,13 +41,51 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.tp_abi_version() == 2
+    assert lib.tp_abi_version() == 3
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.tp_status_string(code).decode() == name
 
 
 def _err(lib):
     return lib.tp_last_error_message().decode()
+
+
+# ------------------------------------------------------- fused FFN middle
+def sw(lib, g=A, ldg=512, u=B, ldu=512, dt=0, m=64, k=512, kind=0, y=C, ldy=512, s=D):
+    return lib.tp_swiglu_rotate(g, ldg, u, ldu, dt, m, k, kind, y, ldy, s, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=300, ldg=304, ldu=304, ldy=304), 3),
+    (dict(k=0), 2),
+    (dict(m=-1), 2),
+    (dict(g=0), 1),
+    (dict(u=0), 1),
+    (dict(y=0), 1),
+    (dict(s=0), 1),
+    (dict(ldg=500), 4),
+    (dict(ldu=511), 4),
+    (dict(ldy=256), 4),
+    (dict(g=A + 8), 5),
+    (dict(ldy=513), 5),
+    (dict(kind=1, ldy=500), 4),
+    (dict(dt=3), 6),
+    (dict(kind=2), 11),
+    (dict(y=A + 4096), 10),
+    (dict(s=C + 64), 10),
+    (dict(kind=1, y=B + 1024), 10),
+    (dict(ldu=2 ** 62), 8),
+])
+def test_swiglu_rotate_refusals(lib, kw, status):
+    assert sw(lib, **kw) == status, _err(lib)
+    assert _err(lib)
+
+
+def test_swiglu_rotate_empty_and_optional_scales(lib):
+    assert sw(lib, m=0) == 0
+    assert sw(lib, m=0, kind=1, s=0, ldy=512) == 0          # bf16 rows: no scales
+    assert sw(lib, m=0, u=A, ldu=512) == 0                  # gate and up may overlap
+    assert sw(lib, m=0, dt=1, ldg=1024, u=A + 1024, ldu=1024) == 0  # column halves of one [m, 2k] bf16 buffer
 
 
 # --------------------------------------------------- rotate-quantize weights
