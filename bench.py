@@ -57,6 +57,9 @@ def parse():
                         "the step's shapes, as context for the roofline fractions (one JSON line per shape)")
     p.add_argument("--only", default=None,
                    help="run only the launches whose name contains this text (for counter profiling)")
+    p.add_argument("--no-next", action="store_true", help="skip the rows measured beside the step (\"next\")")
+    p.add_argument("--next-only", action="store_true",
+                   help="measure only the rows beside the step and print their JSON (for profiling)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                    help="before the step, run a plain device copy of MB MiB (a kernel of known traffic)")
     return p.parse_args()
@@ -216,6 +219,85 @@ def small_m_sweep(args):
         torch.cuda.empty_cache()
 
 
+# ------------------------------------------ rows measured beside the step
+def _time_us(torch, fn, reps=5, inner=10):
+    """Median over `reps` of the mean time of `inner` back-to-back calls (HIP
+    events on the current stream, where the library launches)."""
+    fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(inner):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / inner * 1e3)
+    return float(np.median(out))
+
+
+def next_rows(args, cpu):
+    """The fused FFN middle (SwiGLU -> rotation -> int8 codes or rotated bf16),
+    at the two full-size workloads: its HBM roofline fraction (algorithmic
+    bytes: gate and up read, output written), the unfused two-pass path for
+    context (an ideal SwiGLU pass writing bf16 h at peak HBM bandwidth, plus
+    this library's own rotation pass over h, measured), and the oracle on a
+    bounded row sample."""
+    import torch
+    import int4_quantized_gemm_amd as tp
+    import workloads as W
+    d = torch.device("cuda:0")
+    res = []
+    for w in (W.FFN_MID_W8A8, W.FFN_MID_W4):
+        gu = W.gate_up(w, fused=True).to(d)
+        g, u = gu[:, :w.k], gu[:, w.k:]
+        es = 4 if w.in_dtype == "f32" else 2
+        # h for the unfused second pass: the same values the fused kernel forms
+        # (computed here with plain torch ops, outside the timed region)
+        h = (torch.nn.functional.silu(g.float()) * u.float()).to(torch.bfloat16)
+        if w.out == "i8":
+            y = torch.empty((w.m, w.k), dtype=torch.int8, device=d)
+            sc = torch.empty((w.m,), dtype=torch.float32, device=d)
+            fused = lambda: tp.tp_swiglu_rotate(g, u, out_kind="i8", out=y, scales=sc)
+            second = lambda: tp.tp_quantize_rows_int8(h, qa=y, sa=sc)
+            out_bytes, second_bytes = w.m * w.k + w.m * 4, w.m * w.k * 3 + w.m * 4
+        else:
+            y = torch.empty((w.m, w.k), dtype=torch.bfloat16, device=d)
+            fused = lambda: tp.tp_swiglu_rotate(g, u, out_kind="bf16", out=y)
+            second = lambda: tp.tp_hadamard_rotate_rows(h, out=y)
+            out_bytes, second_bytes = w.m * w.k * 2, w.m * w.k * 4
+        alg = 2 * w.m * w.k * es + out_bytes
+        us = _time_us(torch, fused)
+        us2 = _time_us(torch, second)
+        silu_pass_us = (2 * w.m * w.k * es + w.m * w.k * 2) / (PEAK_HBM_GBS * 1e3)
+        row = {"row": "ffn_middle", "workload": f"{w.name}: M={w.m}, K={w.k}, {w.in_dtype} gate/up -> {w.out}",
+               "us": round(us, 2), "roofline": {"bound": "hbm", "achieved": round(alg / us / 1e3, 1),
+                                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                                "frac": round(alg / us / 1e3 / PEAK_HBM_GBS, 4),
+                                                "algorithmic_bytes": alg},
+               "unfused_us": round(silu_pass_us + us2, 2),
+               "unfused_note": f"ideal SwiGLU pass at peak HBM ({silu_pass_us:.1f} us) + measured rotation pass over "
+                               f"bf16 h ({us2:.1f} us, {second_bytes / us2 / 1e3:.0f} GB/s)"}
+        del gu, g, u, h, y
+        if cpu:
+            rows = 256
+            g64, u64 = (t.double().numpy() for t in W.gate_up(w, rows=rows))
+            import oracle
+            fn = (lambda: oracle.ffn_middle_int8(g64, u64)) if w.out == "i8" else \
+                (lambda: oracle.bf16_round(oracle.ffn_middle_rotated(g64, u64)))
+            times = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                fn()
+                times.append(time.perf_counter() - t0)
+            dt = float(np.median(times))
+            row["cpu_baseline"] = {"value": round(alg * rows / w.m / dt / 1e9, 3), "unit": "GB/s",
+                                   "kind": "oracle", "sample": f"first {rows} rows, median of 3 ({dt:.2f} s)"}
+        res.append(row)
+    return res
+
+
 # ------------------------------------------- platform library, for context only
 def library_reference(args):
     """The platform's own GEMMs on the step's shapes: torch._int_mm (int8 x
@@ -274,6 +356,9 @@ def main():
         return
     if args.library_reference:
         library_reference(args)
+        return
+    if args.next_only:
+        print(json.dumps({"next": next_rows(args, cpu=not args.no_cpu_baseline)}), flush=True)
         return
 
     import torch
@@ -416,6 +501,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    if not args.no_next and not args.only:
+        result["next"] = next_rows(args, cpu=not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
 
 

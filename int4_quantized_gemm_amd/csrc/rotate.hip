@@ -264,32 +264,41 @@ struct RowSrc {
     tp::load8d(x + r * ldx + c, v);
   }
   __device__ __forceinline__ void load16(int64_t r, int64_t c, Raw16<T>& raw) const { raw.load(x + r * ldx + c); }
+  // Two-phase form of load16: fetch issues the loads, finish produces the
+  // raw words (here the loaded words themselves).
+  typedef Raw16<T> stash_t;
+  __device__ __forceinline__ void fetch(int64_t r, int64_t c, stash_t& st) const { st.load(x + r * ldx + c); }
+  __device__ __forceinline__ void finish(int64_t, int64_t, const stash_t& st, Raw16<T>& raw) const { raw = st; }
 };
 
-// bf16 bits of silu(g) * u = g u / (1 + e^-g), rounded once (to nearest even)
-// from the real value: the SwiGLU feed-forward's hidden activation, a bf16
-// tensor (tensai docs, "画像生成", section "何が走るか": every block is
-// attention plus a SwiGLU feed-forward; TensorFold pull request #948: bf16
-// activations rounded where the reference rounds them).
+// The SwiGLU feed-forward's hidden activation h = bf16(silu(g) * u), silu(x)
+// = x / (1 + e^-x), rounded once (to nearest even) from its fp64 evaluation
+// (tensai docs, "画像生成", section "何が走るか": every block is attention plus
+// a SwiGLU feed-forward; TensorFold pull request #948: bf16 activations
+// rounded where the reference rounds them).
 //
-// fp32 first: e = v_exp_f32(-g log2 e), h = (g u) v_rcp_f32(1 + e). Relative
-// error, to first order: |g| 2^-24 from the rounded exponent argument and
-// |g| 2^-25 from the rounded log2 e, 2^-23 each from v_exp_f32 and v_rcp_f32,
-// 2^-24 each from 1 + e, g u and the last product: below (|g| + 8) 2^-24. With
-// h in [2^E, 2^(E+1)) the real value is then within (|g| + 8) fp32 ulps of h,
-// and rounding to bf16 depends only on where the low 16 bits of h sit against
-// the midpoint 0x8000; when they are farther than 4 (|g| + 8) + 8 ulps from it
-// (a 4x margin), h rounds like the real value. Otherwise, and for |g| > 64,
-// |h| < 2^-100 or non-finite h, the value is recomputed in fp64 and rounded
-// to bf16 through fp32 with round-to-odd (no double rounding).
-__device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
+// fp32 first: e = v_exp_f32(-g * fl(log2 e)), h = (g u) v_rcp_f32(1 + e).
+// Relative error, to first order, with u = 2^-24: the exponent argument is
+// off by at most |g log2 e| (u + 2^-26.2) (the product and the rounded log2 e),
+// which makes e off by |g| (u + 2^-26.2) relative; v_exp_f32 and v_rcp_f32 add
+// 2u each, 1 + e, g u and the last product u each: below (1.25 |g| + 8) u in
+// all. For a normal h in [2^E, 2^(E+1)) that is under 1.25 |g| + 8 fp32 ulps,
+// and bf16 rounding only depends on where the low 16 bits of h sit against the
+// midpoint 0x8000: when they are more than 2.5 |g| + 20 ulps away (twice the
+// bound, plus 4), h rounds like its fp64 evaluation. swiglu_fast returns the
+// bf16 bits and whether that holds (false also for |g| > 64 and for h not a
+// normal number); swiglu_exact redoes an element in fp64 and rounds it to bf16
+// through fp32 with round-to-odd (no double rounding).
+__device__ __forceinline__ uint32_t swiglu_fast(float g, float u, bool& ok) {
   const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
   const float h = (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
   const uint32_t b = __builtin_bit_cast(uint32_t, h);
-  const float ag = fabsf(g), ah = fabsf(h);
-  const float dist = fabsf((float)((int)(b & 0xFFFFu) - 0x8000));
-  if (ag <= 64.f && ah >= 0x1p-100f && ah < 0x1p127f && dist > 4.f * (ag + 8.f) + 8.f)
-    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  const float dist = (float)((int)(b & 0xFFFFu) - 0x8000);
+  ok = __builtin_isnormal(h) && fabsf(g) <= 64.f && fabsf(dist) > fmaf(fabsf(g), 2.5f, 20.f);
+  return (b + 0x8000u) >> 16;  // not a tie when ok: no even-rule needed
+}
+
+__device__ __noinline__ uint32_t swiglu_exact(float g, float u) {
   const double hd = ((double)g * (double)u) / (1.0 + exp(-(double)g));
   if (hd != hd) return 0x7FC0u;
   const float f = __double2float_rz(hd);
@@ -299,7 +308,10 @@ __device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
 }
 
 // h = bf16(silu(g) * u) of a gate and an up buffer ([rows, k], both fp32 or
-// both bf16), element by element.
+// both bf16), element by element. Elements the fp32 shortcut cannot decide
+// are collected in a per-lane mask and redone afterwards, one at a time, from
+// reloaded inputs, so a wave pays for the fp64 path once per round of such
+// elements rather than once per element position.
 template <typename T>
 struct SwigluSrc {
   typedef uint16_t raw_elem;
@@ -307,16 +319,50 @@ struct SwigluSrc {
   int64_t ldg;
   const T* u;
   int64_t ldu;
-  __device__ __forceinline__ void bits8(int64_t r, int64_t c, uint32_t (&hb)[8]) const {
-    float gv[8], uv[8];
-    tp::load8(g + r * ldg + c, gv);
-    tp::load8(u + r * ldu + c, uv);
+  template <int N>
+  __device__ __forceinline__ void bits(int64_t r, int64_t c, uint32_t (&hb)[N]) const {
+    float gv[N], uv[N];
+    const T* gp = g + r * ldg + c;
+    const T* up = u + r * ldu + c;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) hb[j] = swiglu_bf16(gv[j], uv[j]);
+    for (int j = 0; j < N; j += 8) {
+      tp::load8(gp + j, *reinterpret_cast<float(*)[8]>(&gv[j]));
+      tp::load8(up + j, *reinterpret_cast<float(*)[8]>(&uv[j]));
+    }
+    compute(r, c, gv, uv, hb);
+  }
+  template <int N>
+  __device__ __forceinline__ void compute(int64_t r, int64_t c, const float (&gv)[N], const float (&uv)[N],
+                                          uint32_t (&hb)[N]) const {
+    const T* gp = g + r * ldg + c;
+    const T* up = u + r * ldu + c;
+    uint32_t redo = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      bool ok;
+      hb[j] = swiglu_fast(gv[j], uv[j], ok);
+      redo |= ok ? 0u : (1u << j);
+    }
+    while (redo) {
+      const int j = __builtin_ctz(redo);
+      redo &= redo - 1;
+      float gj[8], uj[8];
+      tp::load8(gp + (j & ~7), gj);
+      tp::load8(up + (j & ~7), uj);
+      float gs = gj[0], us = uj[0];
+#pragma unroll
+      for (int t = 1; t < 8; ++t) {
+        gs = (t == (j & 7)) ? gj[t] : gs;
+        us = (t == (j & 7)) ? uj[t] : us;
+      }
+      const uint32_t v = swiglu_exact(gs, us);
+#pragma unroll
+      for (int t = 0; t < N; ++t) hb[t] = (t == j) ? v : hb[t];
+    }
   }
   __device__ __forceinline__ void load8(int64_t r, int64_t c, float (&v)[8]) const {
     uint32_t hb[8];
-    bits8(r, c, hb);
+    bits(r, c, hb);
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = __builtin_bit_cast(float, hb[j] << 16);
   }
@@ -327,14 +373,31 @@ struct SwigluSrc {
     for (int j = 0; j < 8; ++j) v[j] = (double)f[j];
   }
   __device__ __forceinline__ void load16(int64_t r, int64_t c, Raw16<uint16_t>& raw) const {
-    uint32_t lo[8], hi[8];
-    bits8(r, c, lo);
-    bits8(r, c + 8, hi);
+    uint32_t hb[16];
+    bits(r, c, hb);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      raw.w[i] = lo[2 * i] | (lo[2 * i + 1] << 16);
-      raw.w[4 + i] = hi[2 * i] | (hi[2 * i + 1] << 16);
+    for (int i = 0; i < 8; ++i) raw.w[i] = hb[2 * i] | (hb[2 * i + 1] << 16);
+  }
+  // Two-phase form of load16: fetch issues the loads of g and u, finish
+  // computes h (so a kernel can have several groups' loads in flight).
+  struct stash_t {
+    Raw16<T> g, u;
+  };
+  __device__ __forceinline__ void fetch(int64_t r, int64_t c, stash_t& st) const {
+    st.g.load(g + r * ldg + c);
+    st.u.load(u + r * ldu + c);
+  }
+  __device__ __forceinline__ void finish(int64_t r, int64_t c, const stash_t& st, Raw16<uint16_t>& raw) const {
+    float gv[16], uv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      gv[j] = st.g.get(j);
+      uv[j] = st.u.get(j);
     }
+    uint32_t hb[16];
+    compute(r, c, gv, uv, hb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) raw.w[i] = hb[2 * i] | (hb[2 * i + 1] << 16);
   }
 };
 
@@ -387,11 +450,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                                                       int groups, int rotate, int8_t* __restrict__ q, int64_t ldq,
                                                       float* __restrict__ scales) {
   typedef typename Src::raw_elem TIn;
+  constexpr int NU = 3;  // groups per 16-lane set
+  constexpr int NWB = 4;  // waves per block
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int set = lane >> 4, l16 = lane & 15;
-  __shared__ __align__(16) uint8_t lds[16 * RQ_ROW_BYTES];
-  __shared__ float red[2][4];
-  __shared__ double red64[4];
+  __shared__ __align__(16) uint8_t lds[4 * NWB * RQ_ROW_BYTES];
+  __shared__ float red[2][NWB];
+  __shared__ double red64[NWB];
   uint8_t* mybuf = lds + (wave * 4 + set) * RQ_ROW_BYTES;
   float* fbuf = reinterpret_cast<float*>(mybuf);
   int64_t row;
@@ -403,27 +468,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     ge = groups;
   } else {
     row = blockIdx.x;
-    const int gpw = (groups + 3) / 4;
+    const int gpw = (groups + WPR - 1) / WPR;
     gb = min(groups, wave * gpw);
     ge = min(groups, gb + gpw);
   }
 
   // Load every group of this wave (up to 3 per 16-lane row) and transform it.
-  Raw16<TIn> raw[3];
-  float v[3][16];
-  float bnd[3];
-  bool has[3];
+  Raw16<TIn> raw[NU];
+  float v[NU][16];
+  float bnd[NU];
+  bool has[NU];
+  {
+    typename Src::stash_t st[NU];
 #pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    has[u] = gb + set + 4 * u < ge;
-    if (has[u])
-      src.load16(row, (int64_t)(gb + set + 4 * u) * 256 + l16 * 16, raw[u]);
-    else
-      raw[u].zero();
+    for (int u = 0; u < NU; ++u) {
+      has[u] = gb + set + 4 * u < ge;
+      if (has[u]) src.fetch(row, (int64_t)(gb + set + 4 * u) * 256 + l16 * 16, st[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (has[u])
+        src.finish(row, (int64_t)(gb + set + 4 * u) * 256 + l16 * 16, st[u], raw[u]);
+      else
+        raw[u].zero();
+    }
   }
   float amax = 0.f, bmax = 0.f;
 #pragma unroll
-  for (int u = 0; u < 3; ++u) {
+  for (int u = 0; u < NU; ++u) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[u][i] = raw[u].get(i);
     bnd[u] = 0.f;
@@ -451,14 +523,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
   bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
   bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-  if constexpr (WPR == 4) {
+  if constexpr (WPR > 1) {
     if (lane == 0) {
       red[0][wave] = amax;
       red[1][wave] = bmax;
     }
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    bmax = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    amax = red[0][0];
+    bmax = red[1][0];
+#pragma unroll
+    for (int w = 1; w < WPR; ++w) {
+      amax = fmaxf(amax, red[0][w]);
+      bmax = fmaxf(bmax, red[1][w]);
+    }
   }
 
   // Exact row maximum (unnormalized): the exact value of every element that
@@ -486,13 +563,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       }
     };
     scan(std::integral_constant<int, 0>{});
-    scan(std::integral_constant<int, 1>{});
-    scan(std::integral_constant<int, 2>{});
+    if constexpr (NU > 1) scan(std::integral_constant<int, 1>{});
+    if constexpr (NU > 2) scan(std::integral_constant<int, 2>{});
     m_ex = wave_max(m_ex);
-    if constexpr (WPR == 4) {
+    if constexpr (WPR > 1) {
       if (lane == 0) red64[wave] = m_ex;
       __syncthreads();
-      m_ex = fmax(fmax(red64[0], red64[1]), fmax(red64[2], red64[3]));
+      m_ex = red64[0];
+#pragma unroll
+      for (int w = 1; w < WPR; ++w) m_ex = fmax(m_ex, red64[w]);
     }
     amax_ex = m_ex;
   }
@@ -545,8 +624,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     if (has[U]) *reinterpret_cast<uint4*>(qr + (int64_t)(gb + set + 4 * U) * 256 + l16 * 16) = w4;
   };
   codes(std::integral_constant<int, 0>{});
-  codes(std::integral_constant<int, 1>{});
-  codes(std::integral_constant<int, 2>{});
+  if constexpr (NU > 1) codes(std::integral_constant<int, 1>{});
+  if constexpr (NU > 2) codes(std::integral_constant<int, 2>{});
   if (lane == 0 && (WPR == 1 || wave == 0)) scales[row] = s;
 }
 
