@@ -49,6 +49,9 @@ the design notes):
   R15 SwiGLU(g, u) = silu(g) * u, silu(x) = x / (1 + e^-x); its output h is
       bf16, rounded once from the real value (oracle/ffn.py).
   R16 h enters the down projection like any other activation.
+  R18 W4A8: the 4-bit weights (one scale per row and 256-group) against the
+      per-row int8 activations of R9: exact integer sums per group, then
+      y = sa[m] * sum_g s[n, g] * acc_g.
 
 Parity pins live in tests/test_oracle.py; planted-fault controls in
 tests/test_controls.py.
@@ -65,7 +68,7 @@ from .quantize import (
     dequantize_int8,
     dequantize_int4,
 )
-from .products import qgemm_w8, qgemm_w4, qgemm_w8a8, int_accumulate
+from .products import qgemm_w8, qgemm_w4, qgemm_w8a8, qgemm_w4a8, int_accumulate, group_accumulate
 from .ffn import silu_mul, swiglu_bf16, ffn_middle_int8, ffn_middle_rotated
 
 __all__ = [
@@ -84,6 +87,8 @@ __all__ = [
     "swiglu_bf16",
     "ffn_middle_int8",
     "ffn_middle_rotated",
+    "qgemm_w4a8",
+    "group_accumulate",
     "qgemm_w8",
     "qgemm_w4",
     "qgemm_w8a8",

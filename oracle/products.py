@@ -6,7 +6,8 @@ Source: tensai docs, "画像生成" (image generation), section "幅とメモリ
 (width and memory): because the per-group rotation is orthogonal, multiplying
 the rotated input by the rotated weight gives the original product up to
 quantization error; section "GPU": the device quantizes each product's
-activations (reading R9 for W8A8).
+activations (reading R9 for W8A8). The same section's 4-bit width ("-q4"),
+combined with those device-quantized activations, gives W4A8 (reading R18).
 """
 
 import numpy as np
@@ -17,6 +18,7 @@ from .quantize import (
     dequantize_int4,
     dequantize_int8,
     quantize_activations_int8,
+    unpack_int4,
 )
 
 
@@ -70,4 +72,30 @@ def qgemm_w8a8(x, q, sw, rotate=True):
     qa, sa = quantize_activations_int8(x, rotate=rotate)
     acc = int_accumulate(qa, q)
     y = acc.astype(np.float64) * sa.astype(np.float64)[:, None] * np.asarray(sw, dtype=np.float64)[None, :]
+    return y, acc, qa, sa
+
+
+def group_accumulate(qa, q, group=256):
+    """Exact integer accumulators per K-group, ACC[g, m, n] = sum over k in
+    group g of qa[m, k] * q[n, k] (int64, [K/group, M, N])."""
+    qa = np.asarray(qa)
+    q = np.asarray(q)
+    k = qa.shape[1]
+    return np.stack([int_accumulate(qa[:, g:g + group], q[:, g:g + group]) for g in range(0, k, group)])
+
+
+def qgemm_w4a8(x, packed, s, rotate=True):
+    """W4A8 product (reading R18): per-row int8 activations as in W8A8 (R9),
+    int4 weights with one scale per (row, 256-group) (R3, R6, R7):
+
+        y[m, n] = sa[m] * sum_g s[n, g] * ACC[g, m, n]
+
+    with ACC the exact per-group integer accumulators, in fp64. Returns
+    (y fp64 [M, N], acc int64 [K/256, M, N], qa int8 [M, K], sa fp32 [M]).
+    """
+    qa, sa = quantize_activations_int8(x, rotate=rotate)
+    q = unpack_int4(packed)
+    acc = group_accumulate(qa, q)
+    sg = np.asarray(s, dtype=np.float64).T  # [G, N]
+    y = np.einsum("gmn,gn->mn", acc.astype(np.float64), sg) * sa.astype(np.float64)[:, None]
     return y, acc, qa, sa

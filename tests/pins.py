@@ -380,3 +380,60 @@ def check_ffn_middle(ffn_middle_int8, ffn_middle_rotated, quantize_activations_i
     q1, s1 = ffn_middle_int8(gg, uu)
     q2, s2 = quantize_activations_int8(bf16_round(gg * uu / (1 + np.exp(-gg))), rotate=True)
     assert np.array_equal(q1, q2) and np.array_equal(s1, s2), "not the quantized rotation of bf16(silu(g) u)"
+
+
+# ------------------------------------------------------------------- W4A8
+def check_w4a8(qgemm_w4a8, qgemm_w8a8, quantize_weights_int4, unpack_int4, pack_int4, rotate_groups,
+               hadamard_matrix, seed=25):
+    """W4A8 (reading R18): y = sa[m] * sum_g s[n, g] * acc_g[m, n].
+
+    * pure-Python loops over the quantized operands on tiny shapes (codes,
+      per-group accumulators and output);
+    * with one scale for all groups of a weight row, W4A8 is the W8A8 product
+      of the same codes with that per-row scale;
+    * planted integers: X = X' Q with integer X' (row maximum 127 c, c a power
+      of two) and integer int4 codes with power-of-two group scales give
+      qa = X', sa = c and y in closed form, exactly.
+    """
+    rng = np.random.default_rng(seed)
+    for m, n, k in ((3, 5, 256), (4, 3, 768)):
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        x[:, 5] *= 30.0
+        w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+        p4, s4 = quantize_weights_int4(w)
+        q4 = unpack_int4(p4)
+        y, acc, qa, sa = qgemm_w4a8(x, p4, s4)
+        assert acc.shape == (k // 256, m, n)
+        for i in range(m):
+            for j in range(n):
+                tot = 0.0
+                for g in range(k // 256):
+                    a = sum(int(qa[i, t]) * int(q4[j, t]) for t in range(256 * g, 256 * g + 256))
+                    assert acc[g, i, j] == a, "w4a8 group accumulator"
+                    tot += float(s4[j, g]) * a
+                ref = tot * float(sa[i])
+                assert abs(y[i, j] - ref) <= 1e-12 * max(1e-30, abs(ref)) + 1e-300, "w4a8 output"
+    # equal group scales: the W8A8 product of the same codes
+    x = rng.standard_normal((5, 512))
+    codes = rng.integers(-7, 8, size=(4, 512))
+    c = np.float32([0.5, 0.003, 1.25, 7.0])
+    y4, _, qa4, sa4 = qgemm_w4a8(x, pack_int4(codes), np.repeat(c[:, None], 2, axis=1))
+    y8, _, qa8, sa8 = qgemm_w8a8(x, codes.astype(np.int8), c)
+    assert np.array_equal(qa4, qa8) and np.array_equal(sa4, sa8)
+    assert np.allclose(y4, y8, rtol=1e-14, atol=0), "equal group scales must give the W8A8 product"
+    # planted integers
+    Q = hadamard_matrix(256) / 16.0
+    xv = rng.integers(-127, 128, size=(3, 512)).astype(np.float64)
+    xv[:, 7] = 127.0
+    cx = np.array([1.0, 0.25, 8.0])
+    x = np.concatenate([(xv * cx[:, None])[:, g * 256:(g + 1) * 256] @ Q for g in range(2)], axis=1)
+    wq = rng.integers(-7, 8, size=(2, 512))
+    ws = np.float32([[0.5, 2.0], [0.125, 4.0]])
+    y, acc, qa, sa = qgemm_w4a8(x, pack_int4(wq), ws)
+    assert np.array_equal(qa.astype(np.int64), xv.astype(np.int64)), "planted activation codes"
+    assert np.array_equal(sa.astype(np.float64), cx), "planted activation scales"
+    for i in range(3):
+        for j in range(2):
+            want = cx[i] * sum(float(ws[j, g]) * sum(int(xv[i, t]) * int(wq[j, t]) for t in range(256 * g, 256 * g + 256))
+                               for g in range(2))
+            assert y[i, j] == want, "planted W4A8 output"

@@ -177,3 +177,26 @@ def test_ffn_middle_unrounded_caught():
     with pytest.raises(AssertionError):
         pins.check_ffn_middle(unrounded, oracle.ffn_middle_rotated, oracle.quantize_activations_int8,
                               oracle.bf16_round, oracle.hadamard_matrix)
+
+
+# ------------------------------------------------------------------ W4A8
+def _w4a8_with(fold):
+    def f(x, packed, s, rotate=True):
+        qa, sa = oracle.quantize_activations_int8(x, rotate=rotate)
+        acc = oracle.group_accumulate(qa, oracle.unpack_int4(packed))
+        y = fold(acc.astype(np.float64), np.asarray(s, dtype=np.float64), sa.astype(np.float64))
+        return y, acc, qa, sa
+    return f
+
+
+@pytest.mark.parametrize("fold", [
+    lambda acc, s, sa: np.einsum("gmn,n->mn", acc, s[:, 0]) * sa[:, None],          # first group's scale only
+    lambda acc, s, sa: np.einsum("gmn,gn->mn", acc, np.roll(s.T, 1, axis=0)) * sa[:, None],  # group index off by one
+    lambda acc, s, sa: np.einsum("gmn,gn->mn", acc, s.T),                            # activation scale dropped
+    lambda acc, s, sa: np.einsum("gmn,gn->mn", acc, s.T) * sa[None, :acc.shape[2]] if acc.shape[1] == acc.shape[2]
+    else np.einsum("gmn,gn->mn", acc, s.T) * sa.mean(),                              # wrong activation scale
+])
+def test_w4a8_fold_faults_caught(fold):
+    with pytest.raises(AssertionError):
+        pins.check_w4a8(_w4a8_with(fold), oracle.qgemm_w8a8, oracle.quantize_weights_int4, oracle.unpack_int4,
+                        oracle.pack_int4, oracle.rotate_groups, oracle.hadamard_matrix)

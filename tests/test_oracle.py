@@ -82,3 +82,8 @@ def test_swiglu():
 def test_ffn_middle():
     pins.check_ffn_middle(oracle.ffn_middle_int8, oracle.ffn_middle_rotated, oracle.quantize_activations_int8,
                           oracle.bf16_round, oracle.hadamard_matrix)
+
+
+def test_w4a8():
+    pins.check_w4a8(oracle.qgemm_w4a8, oracle.qgemm_w8a8, oracle.quantize_weights_int4, oracle.unpack_int4,
+                    oracle.pack_int4, oracle.rotate_groups, oracle.hadamard_matrix)
