@@ -295,7 +295,45 @@ def next_rows(args, cpu):
             row["cpu_baseline"] = {"value": round(alg * rows / w.m / dt / 1e9, 3), "unit": "GB/s",
                                    "kind": "oracle", "sample": f"first {rows} rows, median of 3 ({dt:.2f} s)"}
         res.append(row)
+
+    # NEXT-2: W4A8 on the two K = 12288 down projections (int4 weights with
+    # group scales, per-token int8 activations already quantized).
+    for wl in (W.DIT_DOWN, W.FFN_DOWN):
+        x, w = W.generate(wl)
+        xd = x.to(d)
+        q4, s4 = tp.tp_rotate_quantize_weights(w.to(d), bits=4)
+        qa, sa = tp.tp_quantize_rows_int8(xd)
+        out = torch.empty((wl.m, wl.n), dtype=torch.float32, device=d)
+        ws = torch.empty((max(1, tp.tp_workspace_size(_lib_op_w4a8_pre(), wl.m, wl.n, wl.k, 0)),), dtype=torch.uint8,
+                         device=d)
+        us = _time_us(torch, lambda: tp.tp_qgemm_w4a8_prequantized(qa, sa, q4, s4, out=out, workspace=ws))
+        ops = 2.0 * wl.m * wl.n * wl.k
+        row = {"row": "w4a8", "workload": f"{wl.name}: M={wl.m}, K={wl.k}, N={wl.n}, int8 codes -> fp32",
+               "us": round(us, 2), "roofline": {"bound": "mfma", "achieved": round(ops / us / 1e6, 1),
+                                                "peak": PEAK_TOPS_I8, "unit": "TOP/s",
+                                                "frac": round(ops / us / 1e6 / PEAK_TOPS_I8, 4)}}
+        if cpu:
+            import oracle
+            rows = 64
+            x64 = x[:rows].double().numpy()
+            qh, sh = q4.cpu().numpy(), s4.cpu().numpy()
+            times = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.qgemm_w4a8(x64, qh, sh)
+                times.append(time.perf_counter() - t0)
+            dt = float(np.median(times))
+            row["cpu_baseline"] = {"value": round(2.0 * rows * wl.n * wl.k / dt / 1e12, 5), "unit": "TOP/s",
+                                   "kind": "oracle", "sample": f"first {rows} rows incl. rotation and quantization, "
+                                                               f"median of 3 ({dt:.2f} s)"}
+        res.append(row)
+        del x, w, xd, q4, s4, qa, sa, out, ws
     return res
+
+
+def _lib_op_w4a8_pre():
+    from int4_quantized_gemm_amd import _lib
+    return _lib.TP_OP_QGEMM_W4A8_PREQUANTIZED
 
 
 # ------------------------------------------- platform library, for context only

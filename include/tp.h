@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 3
+#define TP_ABI_VERSION 4
 
 typedef enum tp_status {
   TP_OK = 0,
@@ -86,7 +86,9 @@ typedef enum tp_op {
   TP_OP_QGEMM_W8 = 1,
   TP_OP_QGEMM_W4 = 2,
   TP_OP_QGEMM_W8A8 = 3,
-  TP_OP_QGEMM_W8A8_PREQUANTIZED = 4
+  TP_OP_QGEMM_W8A8_PREQUANTIZED = 4,
+  TP_OP_QGEMM_W4A8 = 5,
+  TP_OP_QGEMM_W4A8_PREQUANTIZED = 6
 } tp_op;
 
 /*
@@ -276,6 +278,46 @@ tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float
                                      int64_t ldq, const float* w_scales, int64_t m, int64_t n, int64_t k,
                                      void* c, tp_dtype c_dtype, int64_t ldc, int32_t* acc_out,
                                      int64_t ld_acc, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/*
+ * tp_qgemm_w4a8 -- the int4 weights of tp_qgemm_w4 (one fp32 scale per row
+ * and 256-group) against per-row int8 activations as in tp_qgemm_w8a8, on the
+ * int8 matrix units (tensai docs, "画像生成", section "幅とメモリ": the 4-bit
+ * "-q4" width; section "GPU": each product's activations are quantized on the
+ * device).
+ *
+ *   a        [m, k] activations (TP_F32 or TP_BF16), row pitch lda; rotated
+ *            first unless a_flags == TP_A_PREROTATED, then quantized exactly as
+ *            tp_quantize_rows_int8.
+ *   q4       packed int4 [n, k/2] (two's complement, even k in the low
+ *            nibble), row pitch ldq_bytes; w_scales fp32 [n, k/256].
+ *   c        [m, n], TP_F32 or TP_BF16, row pitch ldc:
+ *            C[r, c] = (sum_g w_scales[c, g] * float(acc_g[r, c])) * sa[r],
+ *            acc_g the exact int32 sum over group g, the fold in fp32 in group
+ *            order.
+ *   qa_out / sa_out  as in tp_qgemm_w8a8.
+ *   workspace  tp_workspace_size(TP_OP_QGEMM_W4A8, m, n, k, a_flags) bytes.
+ */
+tp_status tp_qgemm_w4a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags,
+                        const uint8_t* q4, int64_t ldq_bytes, const float* w_scales, int64_t m,
+                        int64_t n, int64_t k, void* c, tp_dtype c_dtype, int64_t ldc,
+                        int8_t* qa_out, float* sa_out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * tp_qgemm_w4a8_prequantized -- tp_qgemm_w4a8 on activation codes and scales
+ * the caller already holds (tp_quantize_rows_int8, tp_swiglu_rotate with
+ * TP_FFN_OUT_I8, or an earlier call's qa_out / sa_out).
+ *
+ *   qa       int8 [m, k] codes, row pitch ldqa bytes; sa fp32 [m] scales.
+ *   workspace  tp_workspace_size(TP_OP_QGEMM_W4A8_PREQUANTIZED, m, n, k, 0)
+ *            bytes (0, and NULL allowed, when the product runs unsplit).
+ */
+tp_status tp_qgemm_w4a8_prequantized(const int8_t* qa, int64_t ldqa, const float* sa,
+                                     const uint8_t* q4, int64_t ldq_bytes, const float* w_scales,
+                                     int64_t m, int64_t n, int64_t k, void* c, tp_dtype c_dtype,
+                                     int64_t ldc, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */

@@ -225,3 +225,48 @@ def tp_qgemm_w8a8_prequantized(qa, sa, q, scales, out_dtype=torch.float32, out=N
                                                       scales.data_ptr(), m, n, k, out.data_ptr(), _dt(out), ldc,
                                                       _ptr(acc), ld_acc, _ptr(ws), ws_bytes, _stream(stream)))
     return out
+
+
+def tp_qgemm_w4a8(a, q4, scales, rotate=True, out_dtype=torch.float32, out=None, want_codes=False, workspace=None,
+                  stream=None):
+    """Per-token int8 activations x int4 weights with one scale per (row,
+    256-group); exact int32 sums per group, folded in fp32. Returns C, or
+    (C, qa, sa) when want_codes."""
+    lda = _mat(a, "a")
+    m, k = a.shape
+    n = q4.shape[0]
+    ldq = _mat(q4, "q4")
+    _vec(scales, "w_scales", n * (k // 256))
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    ldc = _mat(out, "out")
+    qa = sa = None
+    if want_codes:
+        qa = torch.empty((m, k), dtype=torch.int8, device=a.device)
+        sa = torch.empty((m,), dtype=torch.float32, device=a.device)
+    flags = TP_A_ROTATE if rotate else TP_A_PREROTATED
+    op = _lib.TP_OP_QGEMM_W4A8_PREQUANTIZED if want_codes else _lib.TP_OP_QGEMM_W4A8
+    ws, ws_bytes = _workspace(op, m, n, k, flags, a.device, workspace)
+    _lib.check(_lib.load().tp_qgemm_w4a8(a.data_ptr(), _dt(a), lda, flags, q4.data_ptr(), ldq, scales.data_ptr(), m,
+                                         n, k, out.data_ptr(), _dt(out), ldc, _ptr(qa), _ptr(sa), _ptr(ws), ws_bytes,
+                                         _stream(stream)))
+    return (out, qa, sa) if want_codes else out
+
+
+def tp_qgemm_w4a8_prequantized(qa, sa, q4, scales, out_dtype=torch.float32, out=None, workspace=None, stream=None):
+    """C = (sum_g s[n, g] * float(qa_g . q4_g^T)) * sa[m] on activation codes
+    already made (tp_quantize_rows_int8, tp_swiglu_rotate)."""
+    ldqa = _mat(qa, "qa")
+    m, k = qa.shape
+    n = q4.shape[0]
+    ldq = _mat(q4, "q4")
+    _vec(sa, "sa", m)
+    _vec(scales, "w_scales", n * (k // 256))
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=qa.device)
+    ldc = _mat(out, "out")
+    ws, ws_bytes = _workspace(_lib.TP_OP_QGEMM_W4A8_PREQUANTIZED, m, n, k, TP_A_PREROTATED, qa.device, workspace)
+    _lib.check(_lib.load().tp_qgemm_w4a8_prequantized(qa.data_ptr(), ldqa, sa.data_ptr(), q4.data_ptr(), ldq,
+                                                      scales.data_ptr(), m, n, k, out.data_ptr(), _dt(out), ldc,
+                                                      _ptr(ws), ws_bytes, _stream(stream)))
+    return out

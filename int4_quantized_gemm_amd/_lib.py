@@ -29,6 +29,7 @@ STATUS_NAMES = {
 TP_F32, TP_BF16 = 0, 1
 TP_A_PREROTATED, TP_A_ROTATE = 0, 1
 TP_OP_QGEMM_W8, TP_OP_QGEMM_W4, TP_OP_QGEMM_W8A8, TP_OP_QGEMM_W8A8_PREQUANTIZED = 1, 2, 3, 4
+TP_OP_QGEMM_W4A8, TP_OP_QGEMM_W4A8_PREQUANTIZED = 5, 6
 TP_FFN_OUT_I8, TP_FFN_OUT_BF16 = 0, 1
 
 _p = ctypes.c_void_p
@@ -49,6 +50,10 @@ SIGNATURES = {
                               _p, _p, _p, _i64, _p, _sz, _p]),
     "tp_qgemm_w8a8_prequantized": (_int, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _i64,
                                            _p, _sz, _p]),
+    "tp_qgemm_w4a8": (_int, [_p, _int, _i64, _int, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _p, _p,
+                             _sz, _p]),
+    "tp_qgemm_w4a8_prequantized": (_int, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _sz,
+                                          _p]),
     "tp_status_string": (ctypes.c_char_p, [_int]),
     "tp_last_error_message": (ctypes.c_char_p, []),
     "tp_abi_version": (_int, []),

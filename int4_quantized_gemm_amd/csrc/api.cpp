@@ -138,8 +138,9 @@ bool workspace_layout(tp_op op, int64_t m, int64_t n, int64_t k, int a_flags, bo
       kind = op == TP_OP_QGEMM_W8 ? tp::GEMM_W8 : tp::GEMM_W4;
       if (a_flags == TP_A_ROTATE && !mul_ok(mk, 2, &l.front)) return false;
       break;
-    case TP_OP_QGEMM_W8A8: {
-      kind = tp::GEMM_W8A8;
+    case TP_OP_QGEMM_W8A8:
+    case TP_OP_QGEMM_W4A8: {
+      kind = op == TP_OP_QGEMM_W8A8 ? tp::GEMM_W8A8 : tp::GEMM_W4A8;
       if (!own_codes) {
         int64_t sa;
         if (!mul_ok(m, 4, &sa)) return false;
@@ -150,6 +151,9 @@ bool workspace_layout(tp_op op, int64_t m, int64_t n, int64_t k, int a_flags, bo
     }
     case TP_OP_QGEMM_W8A8_PREQUANTIZED:
       kind = tp::GEMM_W8A8;
+      break;
+    case TP_OP_QGEMM_W4A8_PREQUANTIZED:
+      kind = tp::GEMM_W4A8;
       break;
     default:
       return false;
@@ -355,28 +359,36 @@ tp_status tp_qgemm_w4(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags,
                      workspace_bytes, stream);
 }
 
-tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags, const int8_t* q, int64_t ldq,
-                        const float* w_scales, int64_t m, int64_t n, int64_t k, void* c, tp_dtype c_dtype,
-                        int64_t ldc, int8_t* qa_out, float* sa_out, int32_t* acc_out, int64_t ld_acc,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// The int8 x int8 (W8A8) and int8 x int4 (W4A8) products on activations the
+// library quantizes first. acc_out is W8A8 only.
+tp_status act8_product(int kind, const void* a, tp_dtype a_dtype, int64_t lda, int a_flags, const void* q,
+                       int64_t ldq, const float* w_scales, int64_t m, int64_t n, int64_t k, void* c,
+                       tp_dtype c_dtype, int64_t ldc, int8_t* qa_out, float* sa_out, int32_t* acc_out,
+                       int64_t ld_acc, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const bool w4 = kind == tp::GEMM_W4A8;
+  const tp_op op = w4 ? TP_OP_QGEMM_W4A8 : TP_OP_QGEMM_W8A8;
   if (a_flags != TP_A_ROTATE && a_flags != TP_A_PREROTATED) return fail(TP_ERR_BAD_FLAGS, "a_flags=%d", a_flags);
   if (!dtype_ok(a_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "a_dtype %d is not TP_F32 or TP_BF16", (int)a_dtype);
   if (!dtype_ok(c_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "c_dtype %d is not TP_F32 or TP_BF16", (int)c_dtype);
   TP_TRY(check_sizes(m, n, k));
-  if (k > INT32_MAX / (127 * 127))
+  if (!w4 && k > INT32_MAX / (127 * 127))
     return fail(TP_ERR_BAD_SHAPE, "k=%lld: the int32 accumulator could overflow (k <= %d)", (long long)k,
                 INT32_MAX / (127 * 127));
   Extent ea, eq, es, ec, eqa, esa, eacc, ew;
   TP_TRY(check_matrix("a", a, m, k * dtype_size(a_dtype), lda, dtype_size(a_dtype), &ea));
-  TP_TRY(check_matrix("q", q, n, k, ldq, 1, &eq));
-  TP_TRY(check_vector("w_scales", w_scales, n, &es));
+  TP_TRY(check_matrix("q", q, n, w4 ? k / 2 : k, ldq, 1, &eq));
+  int64_t ns;
+  if (!mul_ok(n, w4 ? k / 256 : 1, &ns)) return fail(TP_ERR_SIZE_OVERFLOW, "scale count overflows");
+  TP_TRY(check_vector("w_scales", w_scales, ns, &es));
   TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec, dtype_size(c_dtype)));
   const bool own_codes = qa_out && sa_out;
   if (qa_out) TP_TRY(check_matrix("qa_out", qa_out, m, k, k, 1, &eqa));
   if (sa_out) TP_TRY(check_vector("sa_out", sa_out, m, &esa));
   if (acc_out) TP_TRY(check_matrix("acc_out", acc_out, m, n * 4, ld_acc, 4, &eacc, 4));
   WsLayout wl;
-  if (!workspace_layout(TP_OP_QGEMM_W8A8, m, n, k, a_flags, own_codes, &wl))
+  if (!workspace_layout(op, m, n, k, a_flags, own_codes, &wl))
     return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
   TP_TRY(check_workspace(wl, workspace, workspace_bytes, &ew));
   const Extent* outs[] = {&ec, &eqa, &esa, &eacc, &ew};
@@ -395,7 +407,7 @@ tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flag
                                          stream),
                     "activation quantize launch"));
   tp::GemmArgs g{};
-  g.kind = tp::GEMM_W8A8;
+  g.kind = kind;
   g.a = qa;
   g.lda = k;
   g.b = q;
@@ -414,25 +426,29 @@ tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flag
   return hip_status(tp::launch_qgemm(g, stream), "product launch");
 }
 
-tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float* sa, const int8_t* q, int64_t ldq,
-                                     const float* w_scales, int64_t m, int64_t n, int64_t k, void* c,
-                                     tp_dtype c_dtype, int64_t ldc, int32_t* acc_out, int64_t ld_acc,
-                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+tp_status prequantized_product(int kind, const int8_t* qa, int64_t ldqa, const float* sa, const void* q, int64_t ldq,
+                               const float* w_scales, int64_t m, int64_t n, int64_t k, void* c, tp_dtype c_dtype,
+                               int64_t ldc, int32_t* acc_out, int64_t ld_acc, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  const bool w4 = kind == tp::GEMM_W4A8;
+  const tp_op op = w4 ? TP_OP_QGEMM_W4A8_PREQUANTIZED : TP_OP_QGEMM_W8A8_PREQUANTIZED;
   if (!dtype_ok(c_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "c_dtype %d is not TP_F32 or TP_BF16", (int)c_dtype);
   TP_TRY(check_sizes(m, n, k));
-  if (k > INT32_MAX / (127 * 127))
+  if (!w4 && k > INT32_MAX / (127 * 127))
     return fail(TP_ERR_BAD_SHAPE, "k=%lld: the int32 accumulator could overflow (k <= %d)", (long long)k,
                 INT32_MAX / (127 * 127));
   Extent eqa, esa, eq, es, ec, eacc;
   TP_TRY(check_matrix("qa", qa, m, k, ldqa, 1, &eqa));
   TP_TRY(check_vector("sa", sa, m, &esa));
-  TP_TRY(check_matrix("q", q, n, k, ldq, 1, &eq));
-  TP_TRY(check_vector("w_scales", w_scales, n, &es));
+  TP_TRY(check_matrix("q", q, n, w4 ? k / 2 : k, ldq, 1, &eq));
+  int64_t ns;
+  if (!mul_ok(n, w4 ? k / 256 : 1, &ns)) return fail(TP_ERR_SIZE_OVERFLOW, "scale count overflows");
+  TP_TRY(check_vector("w_scales", w_scales, ns, &es));
   TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec, dtype_size(c_dtype)));
   if (acc_out) TP_TRY(check_matrix("acc_out", acc_out, m, n * 4, ld_acc, 4, &eacc, 4));
   WsLayout wl;
   Extent ew;
-  if (!workspace_layout(TP_OP_QGEMM_W8A8_PREQUANTIZED, m, n, k, TP_A_PREROTATED, true, &wl))
+  if (!workspace_layout(op, m, n, k, TP_A_PREROTATED, true, &wl))
     return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
   TP_TRY(check_workspace(wl, workspace, workspace_bytes, &ew));
   const Extent* ins[] = {&eqa, &esa, &eq, &es};
@@ -443,7 +459,7 @@ tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float
     return fail(TP_ERR_BAD_ALIASING, "c, acc_out and the workspace must not overlap");
   if (m == 0 || n == 0) return ok();
   tp::GemmArgs g{};
-  g.kind = tp::GEMM_W8A8;
+  g.kind = kind;
   g.a = qa;
   g.lda = ldqa;
   g.b = q;
@@ -460,6 +476,40 @@ tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float
   g.ld_acc = ld_acc;
   g.part = wl.total > 0 ? workspace : nullptr;
   return hip_status(tp::launch_qgemm(g, stream), "product launch");
+}
+
+}  // namespace
+
+tp_status tp_qgemm_w8a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags, const int8_t* q, int64_t ldq,
+                        const float* w_scales, int64_t m, int64_t n, int64_t k, void* c, tp_dtype c_dtype,
+                        int64_t ldc, int8_t* qa_out, float* sa_out, int32_t* acc_out, int64_t ld_acc,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return act8_product(tp::GEMM_W8A8, a, a_dtype, lda, a_flags, q, ldq, w_scales, m, n, k, c, c_dtype, ldc, qa_out,
+                      sa_out, acc_out, ld_acc, workspace, workspace_bytes, stream);
+}
+
+tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float* sa, const int8_t* q, int64_t ldq,
+                                     const float* w_scales, int64_t m, int64_t n, int64_t k, void* c,
+                                     tp_dtype c_dtype, int64_t ldc, int32_t* acc_out, int64_t ld_acc,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return prequantized_product(tp::GEMM_W8A8, qa, ldqa, sa, q, ldq, w_scales, m, n, k, c, c_dtype, ldc, acc_out,
+                              ld_acc, workspace, workspace_bytes, stream);
+}
+
+tp_status tp_qgemm_w4a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags, const uint8_t* q4,
+                        int64_t ldq_bytes, const float* w_scales, int64_t m, int64_t n, int64_t k, void* c,
+                        tp_dtype c_dtype, int64_t ldc, int8_t* qa_out, float* sa_out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  return act8_product(tp::GEMM_W4A8, a, a_dtype, lda, a_flags, q4, ldq_bytes, w_scales, m, n, k, c, c_dtype, ldc,
+                      qa_out, sa_out, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+tp_status tp_qgemm_w4a8_prequantized(const int8_t* qa, int64_t ldqa, const float* sa, const uint8_t* q4,
+                                     int64_t ldq_bytes, const float* w_scales, int64_t m, int64_t n, int64_t k,
+                                     void* c, tp_dtype c_dtype, int64_t ldc, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  return prequantized_product(tp::GEMM_W4A8, qa, ldqa, sa, q4, ldq_bytes, w_scales, m, n, k, c, c_dtype, ldc,
+                              nullptr, 0, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

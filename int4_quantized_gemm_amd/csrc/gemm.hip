@@ -6,6 +6,8 @@
 //   W4    C = sum_g s[n,g] * (bf16(A'_g) . q_g^T) bf16 MFMA, per-group fp32 rescale
 //   W8A8  acc = qa . q^T (int32, exact); C = (float(acc) * sa[m]) * sw[n]
 //                                                 i8 MFMA 16x16x64, int32 sums
+//   W4A8  C = (sum_g s[n,g] * float(qa_g . q_g^T)) * sa[m]
+//                                                 i8 MFMA, exact int32 per group
 //
 // (tensai docs, "画像生成", section "幅とメモリ": int8 weights with one scale
 // per row, the 4-bit "-q4" width; section "GPU": activations quantized on the
@@ -35,12 +37,16 @@ namespace tp {
 //          tiles (4032x3072 splits into exactly 256): 128-row waves spread
 //          the widening of each code over 8 MFMAs (measured 4032x3072x12288:
 //          391 us with 64x48 waves and a second accumulator set, 277 us);
-//          below that, 128x192 (64x48 waves, 5 stages).
+//          below that, 128x192 (64x48 waves, 5 stages);
+//   W4A8   256x128 (128x32 waves, 5 stages) when that grid fills the CUs at
+//          least twice (the per-group fold keeps a second accumulator set,
+//          and 128-row waves halve the widening per MFMA: 4096x12288x3072
+//          286 -> 235 us), else as W4 below 256x192.
 // The last launch argument is the number of tile-rows an XCD walks together
 // (pp_map_tile): 4 for W8, W4 and wide W8A8 outputs, 8 otherwise (measured:
 // W8 4096x3072x12288 307 -> 257 us from 8 to 4).
 // Smaller outputs: see pick_plan.
-enum KernelCfg { CFG_PP_256x256 = 1, CFG_PP_128x192 = 2, CFG_PP_256x192 = 3 };
+enum KernelCfg { CFG_PP_256x256 = 1, CFG_PP_128x192 = 2, CFG_PP_256x192 = 3, CFG_PP_256x128 = 4 };
 constexpr int64_t W4_MIN_WIDE_TILES = 192;
 constexpr int64_t NUM_CUS = 256;
 
@@ -57,8 +63,10 @@ static PpPlan pick_plan(int kind, int64_t m, int64_t n, int64_t k) {
   const int64_t big = ((m + 255) / 256) * ((n + 255) / 256);
   if (kind == GEMM_W4 && ((m + 255) / 256) * ((n + 191) / 192) >= W4_MIN_WIDE_TILES)
     return PpPlan{CFG_PP_256x192, 1, 0};
+  if (kind == GEMM_W4A8 && big >= 128 && ((m + 255) / 256) * ((n + 127) / 128) >= 2 * NUM_CUS)
+    return PpPlan{CFG_PP_256x128, 1, 0};
   if (big >= 128) {
-    if (kind == GEMM_W4) return PpPlan{CFG_PP_128x192, 1, 0};
+    if (kind == GEMM_W4 || kind == GEMM_W4A8) return PpPlan{CFG_PP_128x192, 1, 0};
     if (kind == GEMM_W8A8 && big < NUM_CUS && ((m + 255) / 256) * ((n + 191) / 192) <= NUM_CUS)
       return PpPlan{CFG_PP_256x192, 1, 0};
     return PpPlan{CFG_PP_256x256, 1, 0};
@@ -86,6 +94,7 @@ void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn)
   switch (pick_cfg(kind, m, n, k)) {
     case CFG_PP_256x256: *bm = 256; *bn = 256; return;
     case CFG_PP_256x192: *bm = 256; *bn = 192; return;
+    case CFG_PP_256x128: *bm = 256; *bn = 128; return;
     default: *bm = 128; *bn = 192; return;
   }
 }
@@ -122,6 +131,9 @@ static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
       if constexpr (KIND == GEMM_W8A8) return launch_pp<KIND, 256, 192, 64, 96, 4>(g, stream);
       if constexpr (KIND == GEMM_W4) return launch_pp<KIND, 256, 192, 128, 48, 3>(g, stream, 4);
       break;
+    case CFG_PP_256x128:
+      if constexpr (KIND == GEMM_W4A8) return launch_pp<KIND, 256, 128, 128, 32, 5>(g, stream, 4);
+      break;
     default:
       return launch_pp<KIND, 128, 192, 64, 48, 5>(g, stream, 4, pl.splits, pl.sps);
   }
@@ -133,6 +145,7 @@ hipError_t launch_qgemm(const GemmArgs& g, hipStream_t stream) {
     case GEMM_W8: return launch_kind<GEMM_W8>(g, stream);
     case GEMM_W4: return launch_kind<GEMM_W4>(g, stream);
     case GEMM_W8A8: return launch_kind<GEMM_W8A8>(g, stream);
+    case GEMM_W4A8: return launch_kind<GEMM_W4A8>(g, stream);
   }
   return hipErrorInvalidValue;
 }

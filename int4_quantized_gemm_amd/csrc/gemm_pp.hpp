@@ -5,6 +5,8 @@
 //   W4    C = sum_g s[n,g] * (bf16(A'_g) . q_g^T)  bf16 MFMA, per-group fp32 rescale
 //   W8A8  acc = qa . q^T (int32, exact); C = (float(acc) * sa[m]) * sw[n]
 //                                                   i8 MFMA 16x16x64, int32 sums
+//   W4A8  acc_g = qa_g . q_g^T (int32, exact per 256-group);
+//         C = (sum_g s[n,g] * float(acc_g)) * sa[m]   i8 MFMA, per-group fp32 fold
 //
 // (tensai docs, "画像生成", section "幅とメモリ": int8 weights with one scale per
 // row and the 4-bit "-q4" width; section "GPU": activations quantized on the
@@ -37,6 +39,12 @@
 // group g = lane/16 the K positions 16g + 8kk + [0, 8); A and B use the same
 // order, so one 16-byte int8 (8-byte int4) weight read serves both k-steps.
 // The i8 kind has one k-step per stage: 16g + [0, 16).
+//
+// W4A8 widening: the same top-nibble bytes (16 * code, exact in int8), put in
+// K order by two byte permutes per 8 codes; the int32 sums of a group are
+// exact (below 2^24 even with the factor 16, so also exact as fp32) and are
+// folded into fp32 with s[n,g] when the group ends. The first MFMA of a group
+// starts from a zero accumulator, so nothing is cleared.
 //
 // W4 widening: one masked AND per 8 codes moves each code to the top nibble of
 // a byte and a signed-byte convert gives 16 * code, so the MFMAs sum 16x the
@@ -96,6 +104,19 @@ __device__ __forceinline__ bf16x8_t pp_widen_i4x8(uint32_t w) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
+// 16 int4 codes (code j of w.x in bits 4j..4j+3, codes 8.. in w.y) -> 16
+// int8 holding 16 * code, in code order.
+__device__ __forceinline__ u32x4_t pp_widen_i4_i8x16(uint2 w) {
+  const uint32_t xh = w.x & 0xF0F0F0F0u, xl = (w.x << 4) & 0xF0F0F0F0u;  // byte j: code 2j+1 / 2j, top nibble
+  const uint32_t yh = w.y & 0xF0F0F0F0u, yl = (w.y << 4) & 0xF0F0F0F0u;
+  u32x4_t o;
+  o.x = __builtin_amdgcn_perm(xh, xl, 0x05010400u);  // bytes xl.0 xh.0 xl.1 xh.1
+  o.y = __builtin_amdgcn_perm(xh, xl, 0x07030602u);  // bytes xl.2 xh.2 xl.3 xh.3
+  o.z = __builtin_amdgcn_perm(yh, yl, 0x05010400u);
+  o.w = __builtin_amdgcn_perm(yh, yl, 0x07030602u);
+  return o;
+}
+
 // 8 int4 codes (one dword, code j in bits 4j..4j+3) -> 8 bf16 holding 16 *
 // code, exact. Each code is moved to the top nibble of a byte, so a signed
 // byte convert (one SDWA instruction) yields 16 * code. mk is 0xF0F0F0F0, or
@@ -113,12 +134,13 @@ __device__ __forceinline__ bf16x8_t pp_widen_i4x8_x16(uint32_t w, uint32_t mk) {
 
 template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE>
 struct PPCfg {
-  static constexpr bool I8 = KIND == GEMM_W8A8;
+  static constexpr bool I8 = KIND == GEMM_W8A8 || KIND == GEMM_W4A8;  // int8 activations, i8 MFMA
+  static constexpr bool B4 = KIND == GEMM_W4 || KIND == GEMM_W4A8;    // packed int4 weights
   static constexpr int NW = 8, NT = 512;
   static constexpr int NWN = BN / WN;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr int AROW = I8 ? 64 : 128;              // A bytes per row per stage
-  static constexpr int BROW = KIND == GEMM_W4 ? 32 : 64;  // B bytes per row per stage
+  static constexpr int BROW = B4 ? 32 : 64;               // B bytes per row per stage
   static constexpr int A_STAGE = BM * AROW, B_STAGE = BN * BROW, STAGE = A_STAGE + B_STAGE;
   static constexpr int A_LOADS = A_STAGE / 1024, LOADS = (A_STAGE + B_STAGE) / 1024;
   static constexpr int HALF = (LOADS + 1) / 2;            // loads owned by each group per stage
@@ -133,7 +155,7 @@ struct PPCfg {
 
 // PARTIAL: the block computes the K stages [blockIdx.y * sps, ...) of its
 // tile and writes the raw sums (int32 for W8A8, unscaled fp32 for W8, scaled
-// fp32 for W4) to part[blockIdx.y][m][n] instead of C; k_qgemm_reduce adds the
+// fp32 for W4 and W4A8, the latter before the activation scale) to part[blockIdx.y][m][n] instead of C; k_qgemm_reduce adds the
 // splits in order and applies the epilogue. sps is a multiple of 4 (whole
 // 256-groups).
 template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE, bool OUT_BF16, bool ACC_OUT, bool PARTIAL>
@@ -180,7 +202,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
       kbytes[i] = AROW;
     } else {
       const int LB = L - A_LOADS;
-      if constexpr (KIND == GEMM_W4) {  // 32 rows x 32 B
+      if constexpr (Cfg::B4) {  // 32 rows x 32 B
         const int row = LB * 32 + (lane >> 1), c = (lane & 1) ^ ((row >> 3) & 1);
         src[i] = B + (int64_t)min(n0 + row, N - 1) * ldb_bytes + c * 16;
       } else {  // 16 rows x 64 B
@@ -219,6 +241,14 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   float cu[KIND == GEMM_W4 ? FN : 1];
   uint32_t mk[KIND == GEMM_W4 ? FN : 1];
   int fix = 0;
+  // W4A8: the fp32 sum of the folded groups (the int32 acc holds one group).
+  f32x4_t tot[KIND == GEMM_W4A8 ? FM : 1][KIND == GEMM_W4A8 ? FN : 1];
+  if constexpr (KIND == GEMM_W4A8) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) tot[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int r16 = lane & 15, g4 = lane >> 4;
   const int groups = K >> 8;
@@ -227,9 +257,10 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   // the compute phase.
   constexpr int NKK = I8 ? 1 : 2;
   u32x4_t fa[NKK][FM];
-  typedef typename std::conditional<KIND == GEMM_W4, uint2, u32x4_t>::type braw_t;
+  typedef typename std::conditional<Cfg::B4, uint2, u32x4_t>::type braw_t;
   braw_t fb[FN];
   float s_nx[KIND == GEMM_W4 ? FN : 1];  // W4: scales of the next group
+  float s_grp[KIND == GEMM_W4A8 ? FN : 1];  // W4A8: scales of the group being folded
 
   // W4: switch the accumulators to the units of the group whose scales are
   // in s_nx (see cu above).
@@ -255,7 +286,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int row = wn0 + j * 16 + r16;
-      if constexpr (KIND == GEMM_W4)
+      if constexpr (Cfg::B4)
         fb[j] = *reinterpret_cast<const uint2*>(bs + row * 32 + ((((g4 >> 1) ^ ((row >> 3) & 1)) << 4) | ((g4 & 1) << 3)));
       else
         fb[j] = *reinterpret_cast<const u32x4_t*>(bs + row * 64 + ((g4 ^ ((row >> 2) & 3)) << 4));
@@ -281,17 +312,49 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
         }
       }
     }
+    if constexpr (KIND == GEMM_W4A8) {
+      if ((ks & 3) == 3) {  // last stage of a 256-group: its scales, for the fold
+        const int g = (ks0 + ks) >> 2;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) s_grp[j] = sw[(int64_t)min(n0 + wn0 + j * 16 + r16, N - 1) * groups + g];
+      }
+    }
     if (ks + NSTAGE - 1 < KS) issue_stage(ks + NSTAGE - 1);
   };
 
   auto compute_phase = [&](int ks) {
-    if constexpr (I8) {
+    if constexpr (KIND == GEMM_W8A8) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, fa[0][i]),
                                                              __builtin_bit_cast(i32x4_t, fb[j]), acc[i][j], 0, 0, 0);
+    } else if constexpr (KIND == GEMM_W4A8) {
+      // A group's first stage starts its sums from zero (the previous group's
+      // were folded at its last stage).
+      const bool first = (ks & 3) == 0;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const i32x4_t b = __builtin_bit_cast(i32x4_t, pp_widen_i4_i8x16(fb[j]));
+        if (first) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, fa[0][i]), b,
+                                                               i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, fa[0][i]), b, acc[i][j],
+                                                               0, 0, 0);
+        }
+      }
+      if ((ks & 3) == 3) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) tot[i][j] += s_grp[j] * __builtin_convertvector(acc[i][j], f32x4_t);
+      }
     } else {
       // W8: the widening of fragment j+1 is interleaved with the MFMAs of
       // fragment j, so one wave's VALU work runs while its matrix
@@ -344,13 +407,13 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   // the loop, and no load is left to interleave with the output stores (on
   // gfx9 loads and stores share one completion counter, so a load waited on
   // between stores would drain every store before it).
-  float ep_sw[KIND == GEMM_W4 ? 1 : FN];
-  float ep_sa[KIND == GEMM_W8A8 ? FM : 1][4];
-  if constexpr (KIND != GEMM_W4 && !PARTIAL) {
+  float ep_sw[Cfg::B4 ? 1 : FN];
+  float ep_sa[I8 ? FM : 1][4];
+  if constexpr (!Cfg::B4 && !PARTIAL) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) ep_sw[j] = sw[min(n0 + wn0 + j * 16 + r16, N - 1)];
   }
-  if constexpr (KIND == GEMM_W8A8 && !PARTIAL) {
+  if constexpr (I8 && !PARTIAL) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -448,6 +511,8 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
           if (col >= N) continue;
           if constexpr (KIND == GEMM_W4)
             pbase[(int64_t)row * N + col] = w4_value(i, j, r);
+          else if constexpr (KIND == GEMM_W4A8)
+            pbase[(int64_t)row * N + col] = tot[i][j][r] * 0.0625f;
           else
             pbase[(int64_t)row * N + col] = acc[i][j][r];
         }
@@ -463,6 +528,8 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   auto value = [&](int i, int j, int r) -> float {
     if constexpr (KIND == GEMM_W8A8) {
       return ((float)acc[i][j][r] * ep_sa[i][r]) * ep_sw[j];
+    } else if constexpr (KIND == GEMM_W4A8) {
+      return (tot[i][j][r] * 0.0625f) * ep_sa[i][r];
     } else if constexpr (KIND == GEMM_W8) {
       return acc[i][j][r] * ep_sw[j];
     } else {
@@ -508,7 +575,7 @@ template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE>
 static hipError_t launch_pp(const GemmArgs& g, hipStream_t stream, int gm = 8, int splits = 1, int sps = 0) {
   const int tiles_m = (int)((g.m + BM - 1) / BM), tiles_n = (int)((g.n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(512);
-  const int64_t lda_bytes = g.lda * (KIND == GEMM_W8A8 ? 1 : 2);
+  const int64_t lda_bytes = g.lda * (PPCfg<KIND, BM, BN, WM, WN, NSTAGE>::I8 ? 1 : 2);
   const uint8_t* a = (const uint8_t*)g.a;
   const uint8_t* b = (const uint8_t*)g.b;
 #define TP_LAUNCH_PP(OB, AO, PA)                                                                                  \

@@ -12,6 +12,7 @@
 //   W8    C = (bf16(A') . q^T) * s[n]
 //   W4    C = sum_g s[n,g] * (bf16(A'_g) . q_g^T), folded per 256-group
 //   W8A8  acc = qa . q^T (int32, exact); C = (float(acc) * sa[m]) * sw[n]
+//   W4A8  (multi-stage kernel only) C = (sum_g s[n,g] * float(acc_g)) * sa[m]
 // (tensai docs, "画像生成", section "幅とメモリ" for the weight formats,
 // section "GPU" for the per-token activation codes.)
 //
@@ -438,7 +439,7 @@ __global__ __launch_bounds__(256) void k_qgemm_reduce(const void* __restrict__ p
     const float* p = reinterpret_cast<const float*>(part);
     float s = p[off];
     for (int sp = 1; sp < splits; ++sp) s += p[sp * plane + off];
-    y = KIND == GEMM_W8 ? s * sw[n] : s;
+    y = KIND == GEMM_W8 ? s * sw[n] : (KIND == GEMM_W4A8 ? s * sa[m] : s);
   }
   if constexpr (OUT_BF16)
     reinterpret_cast<__bf16*>(C)[(int64_t)m * ldc + n] = (__bf16)y;
@@ -463,7 +464,7 @@ constexpr int SK_TARGET_BLOCKS = 512;  // two blocks per CU
 constexpr int SK_MAX_LDS = 64 * 1024;  // activation stage per block (the default dynamic-LDS limit)
 
 inline bool skinny_plan(int kind, int64_t m, int64_t n, int64_t k, SkPlan* p) {
-  if (m < 1 || m > SK_MAX_M || n < 1 || k < 256) return false;
+  if (kind == GEMM_W4A8 || m < 1 || m > SK_MAX_M || n < 1 || k < 256) return false;
   if (m <= GV_MAX_M) {
     *p = SkPlan{true, 1, 1, (int)((n + 15) / 16), 1, (int)(k / 256), 0};
     return (n + 15) / 16 <= INT32_MAX;

@@ -21,21 +21,21 @@ hipError_t launch_rotq_rows(const void* x, bool x_bf16, int64_t ldx, int64_t row
 hipError_t launch_swiglu_rotate(const void* g, int64_t ldg, const void* u, int64_t ldu, bool in_bf16, int64_t m,
                                 int64_t k, bool out_i8, void* y, int64_t ldy, float* scales, hipStream_t stream);
 
-enum GemmKind { GEMM_W8 = 0, GEMM_W4 = 1, GEMM_W8A8 = 2 };
+enum GemmKind { GEMM_W8 = 0, GEMM_W4 = 1, GEMM_W8A8 = 2, GEMM_W4A8 = 3 };
 
 struct GemmArgs {
   int kind;                 // GemmKind
-  const void* a;            // bf16 [m, k] (W8, W4) or int8 [m, k] (W8A8)
+  const void* a;            // bf16 [m, k] (W8, W4) or int8 [m, k] (W8A8, W4A8)
   int64_t lda;              // elements
   const void* b;            // int8 [n, k] or packed int4 [n, k/2]
   int64_t ldb;              // bytes
   const float* w_scales;    // [n] or [n, k/256]
-  const float* a_scales;    // [m] (W8A8) or nullptr
+  const float* a_scales;    // [m] (W8A8, W4A8) or nullptr
   int64_t m, n, k;
   void* c;                  // [m, n]
   bool c_bf16;
   int64_t ldc;              // elements
-  int32_t* acc_out;         // optional int32 [m, n] (W8A8)
+  int32_t* acc_out;         // optional int32 [m, n] (W8A8 only)
   int64_t ld_acc;
   void* part;               // split-K partial sums, qgemm_partial_bytes() bytes (may be null when that is 0)
 };

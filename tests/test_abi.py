@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.tp_abi_version() == 3
+    assert lib.tp_abi_version() == 4
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.tp_status_string(code).decode() == name
 
@@ -258,6 +258,65 @@ def test_prequantized_refusals(lib, kw, status):
 def test_prequantized_large_m_needs_no_workspace(lib):
     assert lib.tp_workspace_size(4, 4096, 9216, 3072, 0) == 0
     assert pq(lib, m=0, ws=0, wsb=0) == 0
+
+
+# ---------------------------------------------------------------- W4A8
+def w4a8(lib, a=A, ad=1, lda=512, flags=1, q=B, ldq=256, s=C, m=4096, n=3072, k=512, c=D, cd=0, ldc=3072, qa=0,
+         sa=0, ws=E, wsb=1 << 30):
+    return lib.tp_qgemm_w4a8(a, ad, lda, flags, q, ldq, s, m, n, k, c, cd, ldc, qa or None, sa or None, ws or None,
+                             wsb, None)
+
+
+def pq4(lib, qa=A, ldqa=4096, sa=C, q=B, ldq=2048, s=C + 65536, m=64, n=256, k=4096, c=D, cd=0, ldc=256, ws=E,
+        wsb=1 << 20):
+    # k = 4096 at m = 64 splits K, so every refusal below is reached before a
+    # launch could be
+    return lib.tp_qgemm_w4a8_prequantized(qa, ldqa, sa, q, ldq, s, m, n, k, c, cd, ldc, ws or None, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=300, lda=304, ldq=256), 3),
+    (dict(k=0), 2),
+    (dict(a=0), 1),
+    (dict(q=0), 1),
+    (dict(s=0), 1),
+    (dict(c=0), 1),
+    (dict(ldq=255), 4),                # packed rows are k/2 bytes
+    (dict(ldq=264), 5),
+    (dict(flags=2), 11),
+    (dict(ad=5), 6),
+    (dict(cd=9), 6),
+    (dict(ws=0, wsb=0), 9),            # the activation codes need a workspace
+    (dict(wsb=100), 9),
+    (dict(c=B + 1024), 10),            # c overlaps the weight codes
+    (dict(qa=E, sa=E + (1 << 20)), 10),  # qa_out overlaps the workspace
+    (dict(ldc=2 ** 61), 8),
+])
+def test_w4a8_refusals(lib, kw, status):
+    assert w4a8(lib, **kw) == status, _err(lib)
+    assert _err(lib)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=0, wsb=0), 9),            # m <= 64: split-K partial sums need a workspace
+    (dict(ldq=2000), 4),
+    (dict(k=300, ldqa=304, ldq=256), 3),
+    (dict(ws=A), 10),
+    (dict(cd=3), 6),
+    (dict(sa=0), 1),
+])
+def test_w4a8_prequantized_refusals(lib, kw, status):
+    assert pq4(lib, **kw) == status, _err(lib)
+
+
+def test_w4a8_workspace_sizes(lib):
+    # front part as W8A8 (codes, then scales at the next 256-byte boundary)
+    assert lib.tp_workspace_size(5, 4096, 3072, 12288, 1) == 4096 * 12288 + 4096 * 4
+    assert lib.tp_workspace_size(6, 4096, 3072, 12288, 0) == 0
+    assert lib.tp_workspace_size(6, 64, 3072, 12288, 0) > 0      # no small-M kernel: split K
+    assert lib.tp_workspace_size(6, 64, 3072, 12288, 0) % (4 * 64 * 3072) == 0
+    assert pq4(lib, m=0, ws=0, wsb=0) == 0
+    assert w4a8(lib, m=0, ws=0, wsb=0) == 0
 
 
 def test_workspace_sizes(lib):
