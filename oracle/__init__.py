@@ -49,6 +49,10 @@ the design notes):
   R15 SwiGLU(g, u) = silu(g) * u, silu(x) = x / (1 + e^-x); its output h is
       bf16, rounded once from the real value (oracle/ffn.py).
   R16 h enters the down projection like any other activation.
+  R19 Undoing a rotated, quantized weight: W_hat = (q * s) . blockdiag(Q)
+      (Q is its own inverse), exact in fp64 (oracle/loader.py).
+  R20 Requantizing to another width is quantizing q * s in the rotated
+      domain (rotation after un-rotation is the identity).
   R18 W4A8: the 4-bit weights (one scale per row and 256-group) against the
       per-row int8 activations of R9: exact integer sums per group, then
       y = sa[m] * sum_g s[n, g] * acc_g.
@@ -70,6 +74,7 @@ from .quantize import (
 )
 from .products import qgemm_w8, qgemm_w4, qgemm_w8a8, qgemm_w4a8, int_accumulate, group_accumulate
 from .ffn import silu_mul, swiglu_bf16, ffn_middle_int8, ffn_middle_rotated
+from .loader import dequantize, dequantize_unrotate, requantize
 
 __all__ = [
     "GROUP",
@@ -83,6 +88,9 @@ __all__ = [
     "unpack_int4",
     "dequantize_int8",
     "dequantize_int4",
+    "dequantize",
+    "dequantize_unrotate",
+    "requantize",
     "silu_mul",
     "swiglu_bf16",
     "ffn_middle_int8",

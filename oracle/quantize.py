@@ -62,26 +62,27 @@ def _scale(amax, qmax):
     return (np.asarray(amax, dtype=np.float64) / float(qmax)).astype(np.float32)
 
 
-def quantize_weights_int8(w):
+def quantize_weights_int8(w, rotate=True):
     """Rotate W [N, K] per 256-group, then per-row symmetric int8 (R3, R7).
 
     Returns (q int8 [N, K], s fp32 [N]) with q = clamp(rint(W'/s), -127, 127),
-    s = fp32(max_k |W'[n, k]| / 127), W' = W . blockdiag(H/16).
+    s = fp32(max_k |W'[n, k]| / 127), W' = W . blockdiag(H/16). With
+    rotate=False, W is taken as already rotated (W' = W).
     """
-    wr = rotate_groups(w)
+    wr = rotate_groups(w) if rotate else np.asarray(w, dtype=np.float64)
     s = _scale(np.max(np.abs(wr), axis=1), INT8_QMAX)
     q = _codes(wr, s[:, None], INT8_QMAX)
     return q.astype(np.int8), s
 
 
-def quantize_weights_int4(w):
+def quantize_weights_int4(w, rotate=True):
     """Rotate W [N, K] per 256-group, then int4 with one scale per (row, group).
 
     Returns (packed uint8 [N, K/2], s fp32 [N, K/256]): codes are
     clamp(rint(W'/s), -7, 7) with s = fp32(max |W'| over the group / 7), packed
-    two per byte (R6).
+    two per byte (R6). With rotate=False, W is taken as already rotated.
     """
-    wr = rotate_groups(w)
+    wr = rotate_groups(w) if rotate else np.asarray(w, dtype=np.float64)
     n, k = wr.shape
     g = wr.reshape(n, k // GROUP, GROUP)
     s = _scale(np.max(np.abs(g), axis=2), INT4_QMAX)

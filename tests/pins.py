@@ -437,3 +437,57 @@ def check_w4a8(qgemm_w4a8, qgemm_w8a8, quantize_weights_int4, unpack_int4, pack_
             want = cx[i] * sum(float(ws[j, g]) * sum(int(xv[i, t]) * int(wq[j, t]) for t in range(256 * g, 256 * g + 256))
                                for g in range(2))
             assert y[i, j] == want, "planted W4A8 output"
+
+
+# ------------------------------------------------------------------ loader
+def check_loader(dequantize_unrotate, requantize, quantize_weights_int8, quantize_weights_int4, pack_int4,
+                 hadamard_matrix, seed=26):
+    """Undoing a rotated, quantized weight and requantizing it (R19, R20).
+
+    * closed form: codes 127 at one position j of a group, scale s, give that
+      group's row 127 s H[j, :] / 16 and zeros elsewhere;
+    * un-rotation undoes the rotation: for quantizer outputs, every 256-group
+      of W_hat is within sqrt(256) s / 2 of W in the 2-norm (the codes' error is
+      at most s / 2 per element in the rotated domain and Q is orthonormal);
+    * requantizing to the same width is the identity on quantizer outputs
+      (int8 and int4);
+    * planted int8 -> int4: codes 18 t with t in [-7, 7] (a 7 in every group)
+      and a power-of-two scale c give t and 18 c;
+    * int4 -> int8 on planted power-of-two group scales, against the R3/R4 rule
+      written out here.
+    """
+    rng = np.random.default_rng(seed)
+    h = hadamard_matrix(256)
+    q = np.zeros((2, 512), dtype=np.int8)
+    q[0, 37] = 127
+    q[1, 256 + 200] = -127
+    s = np.float32([0.5, 1.0 / 127.0])
+    w = dequantize_unrotate(q, s, 8)
+    assert np.array_equal(w[0, :256], 127 * float(s[0]) * h[37] / 16.0) and np.all(w[0, 256:] == 0)
+    assert np.array_equal(w[1, 256:], -127 * float(s[1]) * h[200] / 16.0) and np.all(w[1, :256] == 0)
+    wt = (0.02 * rng.standard_normal((6, 768))).astype(np.float32)
+    wt[:, 11] *= 20.0
+    q8, s8 = quantize_weights_int8(wt)
+    wh = dequantize_unrotate(q8, s8, 8)
+    err = np.linalg.norm((wh - wt).reshape(6, 3, 256), axis=2)
+    assert np.all(err <= 16.0 * s8[:, None] / 2.0 * (1 + 1e-12)), "un-rotation does not undo the rotation"
+    q8b, s8b = requantize(q8, s8, 8, 8)
+    assert np.array_equal(q8b, q8) and np.array_equal(s8b, s8), "int8 -> int8 must be the identity"
+    p4, s4 = quantize_weights_int4(wt)
+    p4b, s4b = requantize(p4, s4, 4, 4)
+    assert np.array_equal(p4b, p4) and np.array_equal(s4b, s4), "int4 -> int4 must be the identity"
+    t = rng.integers(-7, 8, size=(3, 512))
+    t[:, 5] = 7
+    t[:, 300] = -7
+    c = np.float32([0.25, 1.0, 2.0 ** -10])
+    p, sc = requantize((18 * t).astype(np.int8), c, 8, 4)
+    assert np.array_equal(p, pack_int4(t)), "planted int8 -> int4 codes"
+    assert np.array_equal(sc, np.repeat((18 * c)[:, None], 2, axis=1).astype(np.float32)), "planted int4 scales"
+    sg = np.float32([[0.5, 2.0], [0.125, 0.125], [4.0, 1.0]])
+    q8c, s8c = requantize(pack_int4(t), sg, 4, 8)
+    for r in range(3):
+        vals = [int(t[r, j]) * float(sg[r, j // 256]) for j in range(512)]
+        sr = np.float32(max(abs(v) for v in vals) / 127.0)
+        assert s8c[r] == sr, "int4 -> int8 scale"
+        want = [max(-127, min(127, int(np.rint(v / float(sr))))) for v in vals]
+        assert list(q8c[r].astype(int)) == want, "int4 -> int8 codes"

@@ -200,3 +200,34 @@ def test_w4a8_fold_faults_caught(fold):
     with pytest.raises(AssertionError):
         pins.check_w4a8(_w4a8_with(fold), oracle.qgemm_w8a8, oracle.quantize_weights_int4, oracle.unpack_int4,
                         oracle.pack_int4, oracle.rotate_groups, oracle.hadamard_matrix)
+
+
+# ---------------------------------------------------------------- loader
+def _loader_args():
+    return (oracle.quantize_weights_int8, oracle.quantize_weights_int4, oracle.pack_int4, oracle.hadamard_matrix)
+
+
+def test_unrotation_without_normalization_caught():
+    def unrot(q, s, bits):
+        x = oracle.dequantize(q, s, bits)
+        r, k = x.shape
+        return np.matmul(x.reshape(r, k // 256, 256), oracle.hadamard_matrix(256)).reshape(r, k)
+    with pytest.raises(AssertionError):
+        pins.check_loader(unrot, oracle.requantize, *_loader_args())
+
+
+def test_requantize_rotating_again_caught():
+    def req(q, s, bits_in, bits_out):
+        w = oracle.dequantize(q, s, bits_in)
+        return (oracle.quantize_weights_int8(w) if bits_out == 8 else oracle.quantize_weights_int4(w))
+    with pytest.raises(AssertionError):
+        pins.check_loader(oracle.dequantize_unrotate, req, *_loader_args())
+
+
+def test_requantize_int4_scale_index_caught():
+    def req(q, s, bits_in, bits_out):
+        if bits_in == 4:
+            s = np.roll(np.asarray(s), 1, axis=1)
+        return oracle.requantize(q, s, bits_in, bits_out)
+    with pytest.raises(AssertionError):
+        pins.check_loader(oracle.dequantize_unrotate, req, *_loader_args())

@@ -87,3 +87,8 @@ def test_ffn_middle():
 def test_w4a8():
     pins.check_w4a8(oracle.qgemm_w4a8, oracle.qgemm_w8a8, oracle.quantize_weights_int4, oracle.unpack_int4,
                     oracle.pack_int4, oracle.rotate_groups, oracle.hadamard_matrix)
+
+
+def test_loader():
+    pins.check_loader(oracle.dequantize_unrotate, oracle.requantize, oracle.quantize_weights_int8,
+                      oracle.quantize_weights_int4, oracle.pack_int4, oracle.hadamard_matrix)
