@@ -328,6 +328,41 @@ def next_rows(args, cpu):
                                                                f"median of 3 ({dt:.2f} s)"}
         res.append(row)
         del x, w, xd, q4, s4, qa, sa, out, ws
+
+    # NEXT-3: the loader path on the largest weight of the block (gate+up,
+    # 24576 x 3072): undo the int8 codes to fp32, and requantize them to int4.
+    wl = W.DIT_GATEUP
+    _, w = W.generate(wl, rows=1)
+    q8, s8 = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    wh = torch.empty((wl.n, wl.k), dtype=torch.float32, device=d)
+    q4 = torch.empty((wl.n, wl.k // 2), dtype=torch.uint8, device=d)
+    s4 = torch.empty((wl.n, wl.k // 256), dtype=torch.float32, device=d)
+    nk = wl.n * wl.k
+    for name, fn, alg in (
+            ("dequantize_unrotate int8 -> fp32", lambda: tp.tp_dequantize_unrotate(q8, s8, 8, out=wh),
+             nk * (1 + 4) + wl.n * 4),
+            ("requantize int8 -> int4", lambda: tp.tp_requantize_weights(q8, s8, 8, 4, q_out=q4, scales_out=s4),
+             nk * (1 + 0.5) + wl.n * 4 + wl.n * (wl.k // 256) * 4)):
+        us = _time_us(torch, fn)
+        row = {"row": "loader", "workload": f"{name}: {wl.name} weight N={wl.n}, K={wl.k}", "us": round(us, 2),
+               "roofline": {"bound": "hbm", "achieved": round(alg / us / 1e3, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(alg / us / 1e3 / PEAK_HBM_GBS, 4),
+                            "algorithmic_bytes": int(alg)}}
+        if cpu:
+            import oracle
+            rows = 512
+            qh, sh = q8[:rows].cpu().numpy(), s8[:rows].cpu().numpy()
+            f = (lambda: oracle.dequantize_unrotate(qh, sh, 8)) if "unrotate" in name else \
+                (lambda: oracle.requantize(qh, sh, 8, 4))
+            times = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                f()
+                times.append(time.perf_counter() - t0)
+            dt = float(np.median(times))
+            row["cpu_baseline"] = {"value": round(alg * rows / wl.n / dt / 1e9, 3), "unit": "GB/s", "kind": "oracle",
+                                   "sample": f"first {rows} weight rows, median of 3 ({dt:.2f} s)"}
+        res.append(row)
     return res
 
 

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 4
+#define TP_ABI_VERSION 5
 
 typedef enum tp_status {
   TP_OK = 0,
@@ -146,6 +146,40 @@ tp_status tp_hadamard_rotate_rows(const void* x, tp_dtype x_dtype, int64_t m, in
 tp_status tp_quantize_rows_int8(const void* x, tp_dtype x_dtype, int64_t m, int64_t k,
                                 int64_t ldx, int a_flags, int8_t* qa, int64_t ldqa, float* sa,
                                 hipStream_t stream);
+
+/*
+ * tp_dequantize_unrotate -- undo a rotated, quantized weight (tensai docs,
+ * "画像生成", section "チェックポイントの入手": the loader undoes the rotation
+ * and the per-row int8 of a ConvRot checkpoint before quantizing it its own
+ * way). Q = H/16 is its own inverse, so
+ *
+ *   W_hat = (q * s) . blockdiag(Q),
+ *
+ * computed in fp64, which is exact (a group's values are integers times one
+ * scale), and rounded once to w_dtype (RNE).
+ *
+ *   q       bits 8: int8 [n, k] codes, scales fp32 [n];
+ *           bits 4: packed int4 [n, k/2] (two's complement, even k in the
+ *           low nibble), scales fp32 [n, k/256]. Row pitch ldq_bytes.
+ *   w       [n, k], TP_F32 or TP_BF16, row pitch ldw; must not overlap q or
+ *           scales.
+ */
+tp_status tp_dequantize_unrotate(const void* q, int bits, int64_t ldq_bytes, const float* scales,
+                                 int64_t n, int64_t k, void* w, tp_dtype w_dtype, int64_t ldw,
+                                 hipStream_t stream);
+
+/*
+ * tp_requantize_weights -- the codes of width bits_out (8 or 4) for the
+ * weight held as rotated codes of width bits_in (same section: undo, then
+ * quantize). Rotating W_hat again gives q * s back exactly, so this is the
+ * quantization of q * s with the rules of tp_rotate_quantize_weights, without
+ * a transform, in fp64: bit-identical to tp_rotate_quantize_weights on an
+ * exact W_hat. Layouts as in tp_dequantize_unrotate; int8 -> int8 and
+ * int4 -> int4 give back quantizer outputs unchanged.
+ */
+tp_status tp_requantize_weights(const void* q_in, int bits_in, int64_t ldq_in, const float* s_in,
+                                int64_t n, int64_t k, int bits_out, void* q_out, int64_t ldq_out,
+                                float* s_out, hipStream_t stream);
 
 /* out_kind of tp_swiglu_rotate. */
 #define TP_FFN_OUT_I8 0   /* int8 codes [m, k] and fp32 scales [m] */

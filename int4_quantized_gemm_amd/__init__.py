@@ -270,3 +270,39 @@ def tp_qgemm_w4a8_prequantized(qa, sa, q4, scales, out_dtype=torch.float32, out=
                                                       scales.data_ptr(), m, n, k, out.data_ptr(), _dt(out), ldc,
                                                       _ptr(ws), ws_bytes, _stream(stream)))
     return out
+
+
+def tp_dequantize_unrotate(q, scales, bits, out_dtype=torch.float32, out=None, stream=None):
+    """W_hat = (q * s) . blockdiag(H/16): the weight a rotated, quantized
+    checkpoint stands for (exact, rounded once to out_dtype). q: int8 [n, k]
+    with scales [n] (bits 8) or packed uint8 [n, k/2] with scales [n, k/256]
+    (bits 4)."""
+    ldq = _mat(q, "q")
+    n = q.shape[0]
+    k = q.shape[1] * (1 if bits == 8 else 2)
+    _vec(scales, "scales", n * (1 if bits == 8 else k // 256))
+    if out is None:
+        out = torch.empty((n, k), dtype=out_dtype, device=q.device)
+    ldw = _mat(out, "out")
+    _lib.check(_lib.load().tp_dequantize_unrotate(q.data_ptr(), bits, ldq, scales.data_ptr(), n, k, out.data_ptr(),
+                                                  _dt(out), ldw, _stream(stream)))
+    return out
+
+
+def tp_requantize_weights(q, scales, bits_in, bits_out, q_out=None, scales_out=None, stream=None):
+    """Codes and scales of width bits_out for the weight held as (q, scales)
+    of width bits_in (same layouts as tp_rotate_quantize_weights)."""
+    ldq = _mat(q, "q")
+    n = q.shape[0]
+    k = q.shape[1] * (1 if bits_in == 8 else 2)
+    _vec(scales, "scales", n * (1 if bits_in == 8 else k // 256))
+    if q_out is None:
+        q_out = torch.empty((n, k if bits_out == 8 else k // 2), dtype=torch.int8 if bits_out == 8 else torch.uint8,
+                            device=q.device)
+    if scales_out is None:
+        scales_out = torch.empty((n,) if bits_out == 8 else (n, k // 256), dtype=torch.float32, device=q.device)
+    ldo = _mat(q_out, "q_out")
+    _vec(scales_out, "scales_out", n * (1 if bits_out == 8 else k // 256))
+    _lib.check(_lib.load().tp_requantize_weights(q.data_ptr(), bits_in, ldq, scales.data_ptr(), n, k, bits_out,
+                                                 q_out.data_ptr(), ldo, scales_out.data_ptr(), _stream(stream)))
+    return q_out, scales_out

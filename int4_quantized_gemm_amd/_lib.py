@@ -42,6 +42,8 @@ SIGNATURES = {
     "tp_rotate_quantize_weights": (_int, [_p, _int, _i64, _i64, _i64, _int, _p, _i64, _p, _p]),
     "tp_hadamard_rotate_rows": (_int, [_p, _int, _i64, _i64, _i64, _p, _int, _i64, _p]),
     "tp_quantize_rows_int8": (_int, [_p, _int, _i64, _i64, _i64, _int, _p, _i64, _p, _p]),
+    "tp_dequantize_unrotate": (_int, [_p, _int, _i64, _p, _i64, _i64, _p, _int, _i64, _p]),
+    "tp_requantize_weights": (_int, [_p, _int, _i64, _p, _i64, _i64, _int, _p, _i64, _p, _p]),
     "tp_swiglu_rotate": (_int, [_p, _i64, _p, _i64, _int, _i64, _i64, _int, _p, _i64, _p, _p]),
     "tp_workspace_size": (_sz, [_int, _i64, _i64, _i64, _int]),
     "tp_qgemm_w8": (_int, [_p, _int, _i64, _int, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _sz, _p]),

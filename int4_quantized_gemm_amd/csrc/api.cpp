@@ -264,6 +264,46 @@ tp_status tp_quantize_rows_int8(const void* x, tp_dtype x_dtype, int64_t m, int6
                     "activation quantize launch");
 }
 
+namespace {
+
+tp_status check_codes(const char* name, const void* q, int bits, int64_t n, int64_t k, int64_t ldq, const char* sname,
+                      const float* s, Extent* eq, Extent* es) {
+  if (bits != 8 && bits != 4) return fail(TP_ERR_UNSUPPORTED_BITS, "%s: bits=%d is neither 8 nor 4", name, bits);
+  TP_TRY(check_matrix(name, q, n, bits == 8 ? k : k / 2, ldq, 1, eq));
+  int64_t ns;
+  if (!mul_ok(n, bits == 8 ? 1 : k / 256, &ns)) return fail(TP_ERR_SIZE_OVERFLOW, "%s: scale count overflows", sname);
+  return check_vector(sname, s, ns, es);
+}
+
+}  // namespace
+
+tp_status tp_dequantize_unrotate(const void* q, int bits, int64_t ldq_bytes, const float* scales, int64_t n,
+                                 int64_t k, void* w, tp_dtype w_dtype, int64_t ldw, hipStream_t stream) {
+  if (!dtype_ok(w_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "w_dtype %d is not TP_F32 or TP_BF16", (int)w_dtype);
+  TP_TRY(check_sizes(0, n, k));
+  Extent eq, es, ew;
+  TP_TRY(check_codes("q", q, bits, n, k, ldq_bytes, "scales", scales, &eq, &es));
+  TP_TRY(check_matrix("w", w, n, k * dtype_size(w_dtype), ldw, dtype_size(w_dtype), &ew));
+  if (overlaps(ew, eq) || overlaps(ew, es)) return fail(TP_ERR_BAD_ALIASING, "w must not overlap q or scales");
+  if (n == 0) return ok();
+  return hip_status(tp::launch_dequant_unrotate(q, bits, ldq_bytes, scales, n, k, w, w_dtype == TP_BF16, ldw, stream),
+                    "dequantize launch");
+}
+
+tp_status tp_requantize_weights(const void* q_in, int bits_in, int64_t ldq_in, const float* s_in, int64_t n,
+                                int64_t k, int bits_out, void* q_out, int64_t ldq_out, float* s_out,
+                                hipStream_t stream) {
+  TP_TRY(check_sizes(0, n, k));
+  Extent eqi, esi, eqo, eso;
+  TP_TRY(check_codes("q_in", q_in, bits_in, n, k, ldq_in, "s_in", s_in, &eqi, &esi));
+  TP_TRY(check_codes("q_out", q_out, bits_out, n, k, ldq_out, "s_out", s_out, &eqo, &eso));
+  if (overlaps(eqo, eqi) || overlaps(eqo, esi) || overlaps(eso, eqi) || overlaps(eso, esi) || overlaps(eqo, eso))
+    return fail(TP_ERR_BAD_ALIASING, "q_out and s_out must not overlap the inputs or each other");
+  if (n == 0) return ok();
+  return hip_status(tp::launch_requantize(q_in, bits_in, ldq_in, s_in, n, k, bits_out, q_out, ldq_out, s_out, stream),
+                    "requantize launch");
+}
+
 tp_status tp_swiglu_rotate(const void* gate, int64_t ld_gate, const void* up, int64_t ld_up, tp_dtype in_dtype,
                            int64_t m, int64_t k, int out_kind, void* y, int64_t ldy, float* scales,
                            hipStream_t stream) {

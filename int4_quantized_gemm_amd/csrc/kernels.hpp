@@ -16,6 +16,14 @@ hipError_t launch_rotate_rows(const void* x, bool x_bf16, int64_t ldx, void* y, 
 hipError_t launch_rotq_rows(const void* x, bool x_bf16, int64_t ldx, int64_t rows, int64_t k, bool rotate,
                             int bits, void* q, int64_t ldq, float* scales, hipStream_t stream);
 
+// Rotated weight codes (int8 per-row scales, or packed int4 per-group scales):
+// w = (q * s) . blockdiag(H/16) rounded once to fp32 or bf16, and the codes
+// of another width for the same q * s (no transform).
+hipError_t launch_dequant_unrotate(const void* q, int bits, int64_t ldq, const float* scales, int64_t n, int64_t k,
+                                  void* w, bool w_bf16, int64_t ldw, hipStream_t stream);
+hipError_t launch_requantize(const void* q_in, int bits_in, int64_t ldq_in, const float* s_in, int64_t n, int64_t k,
+                             int bits_out, void* q_out, int64_t ldq_out, float* s_out, hipStream_t stream);
+
 // FFN middle: h = bf16(silu(g) * u), rotated per 256-group, then int8 codes
 // with one scale per row (out_i8) or bf16 rows (scales unused).
 hipError_t launch_swiglu_rotate(const void* g, int64_t ldg, const void* u, int64_t ldu, bool in_bf16, int64_t m,

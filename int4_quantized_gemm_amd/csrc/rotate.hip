@@ -12,7 +12,14 @@
 //  * k_rotq_i8_fast      the int8 rows of k_rotq_rows<I8_ROW> in fp32 with an
 //                        exact fallback.
 //
-// Every kernel reads its rows through a source (RowSrc: a buffer; SwigluSrc:
+//  * k_unrotate_rows     y = (q * s) . blockdiag(H/16) in fp64 (exact), rounded
+//                        once: undoing a rotated, quantized weight (section
+//                        "チェックポイントの入手": the loader undoes the
+//                        rotation and the per-row int8 before quantizing
+//                        itself).
+//
+// Every kernel reads its rows through a source (RowSrc: a buffer; DequantSrc:
+// q * s of rotated int8 or int4 codes; SwigluSrc:
 // the FFN middle h = bf16(silu(g) * u) of a gate and an up buffer, computed on
 // the fly, so that the down projection's input is rotated and quantized
 // without a round trip through memory).
@@ -43,6 +50,45 @@ __global__ __launch_bounds__(256) void k_rotate_rows(Src src, TOut* y, int64_t l
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] *= 0.0625f;
   store8(y + row * ldy + col, v);
+}
+
+// Rounds an fp64 value to bf16 (nearest even) with one rounding: through fp32
+// with round-to-odd, which keeps the bits that decide the second rounding.
+__device__ __forceinline__ uint32_t bf16_bits_from_double(double d) {
+  if (d != d) return 0x7FC0u;
+  const float f = __double2float_rz(d);
+  uint32_t fb = __builtin_bit_cast(uint32_t, f);
+  if ((double)f != d) fb |= 1u;
+  return (fb + 0x7FFFu + ((fb >> 16) & 1u)) >> 16;
+}
+
+// The rotation in fp64 with one rounding of the result: exact for sources
+// whose groups are integers times one scale (DequantSrc).
+template <typename Src, typename TOut>
+__global__ __launch_bounds__(256) void k_unrotate_rows(Src src, TOut* y, int64_t ldy, int64_t units, int groups) {
+  const int lane = threadIdx.x & 63;
+  const int lane32 = lane & 31;
+  const int64_t unit = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+  if (unit >= units) return;  // uniform over the half wave that owns the unit
+  const int64_t row = unit / groups;
+  const int64_t col = (unit - row * groups) * 256 + lane32 * 8;
+  double v[8];
+  src.load8d(row, col, v);
+  fwht256_lane8(v, lane32);
+  TOut* out = y + row * ldy + col;
+  if constexpr (std::is_same<TOut, float>::value) {
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (float)(v[j] * 0.0625);
+    store8(out, f);
+  } else {
+    u32x4_t a;
+    a.x = bf16_bits_from_double(v[0] * 0.0625) | (bf16_bits_from_double(v[1] * 0.0625) << 16);
+    a.y = bf16_bits_from_double(v[2] * 0.0625) | (bf16_bits_from_double(v[3] * 0.0625) << 16);
+    a.z = bf16_bits_from_double(v[4] * 0.0625) | (bf16_bits_from_double(v[5] * 0.0625) << 16);
+    a.w = bf16_bits_from_double(v[6] * 0.0625) | (bf16_bits_from_double(v[7] * 0.0625) << 16);
+    *reinterpret_cast<u32x4_t*>(out) = a;
+  }
 }
 
 // ------------------------------------------------------- rotate and quantize
@@ -269,6 +315,34 @@ struct RowSrc {
   typedef Raw16<T> stash_t;
   __device__ __forceinline__ void fetch(int64_t r, int64_t c, stash_t& st) const { st.load(x + r * ldx + c); }
   __device__ __forceinline__ void finish(int64_t, int64_t, const stash_t& st, Raw16<T>& raw) const { raw = st; }
+};
+
+// q * s of rotated weight codes: int8 with one scale per row (BITS 8) or
+// packed int4 with one scale per row and 256-group (BITS 4). Exact in fp64
+// (an 8-bit integer times an fp32 scale). Only the fp64 loads are provided.
+template <int BITS>
+struct DequantSrc {
+  typedef float raw_elem;
+  const uint8_t* q;
+  int64_t ldq;  // bytes
+  const float* s;
+  int groups;
+  __device__ __forceinline__ void load8d(int64_t r, int64_t c, double (&v)[8]) const {
+    if constexpr (BITS == 8) {
+      const double sc = (double)s[r];
+      const uint2 w = *reinterpret_cast<const uint2*>(q + r * ldq + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = (double)(int8_t)(w.x >> (8 * j)) * sc;
+        v[4 + j] = (double)(int8_t)(w.y >> (8 * j)) * sc;
+      }
+    } else {
+      const double sc = (double)s[r * groups + c / 256];
+      const int32_t w = *reinterpret_cast<const int32_t*>(q + r * ldq + c / 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (double)((w << (28 - 4 * j)) >> 28) * sc;
+    }
+  }
 };
 
 // The SwiGLU feed-forward's hidden activation h = bf16(silu(g) * u), silu(x)
@@ -682,6 +756,40 @@ hipError_t launch_rotq_rows(const void* x, bool x_bf16, int64_t ldx, int64_t row
   else
     hipLaunchKernelGGL((k_rotq_rows<RowSrc<float>, MODE_I4_GROUP>), grid, block, 0, stream,
                        RowSrc<float>{(const float*)x, ldx}, rows, groups, rot, (uint8_t*)q, ldq, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_unrotate(const void* q, int bits, int64_t ldq, const float* scales, int64_t n, int64_t k,
+                                  void* w, bool w_bf16, int64_t ldw, hipStream_t stream) {
+  const int groups = (int)(k / 256);
+  const int64_t units = n * groups;
+  const dim3 grid((unsigned)((units + 7) / 8)), block(256);
+#define TP_UNROT(B, TO)                                                                                        \
+  hipLaunchKernelGGL((k_unrotate_rows<DequantSrc<B>, TO>), grid, block, 0, stream,                               \
+                     DequantSrc<B>{(const uint8_t*)q, ldq, scales, groups}, (TO*)w, ldw, units, groups)
+  if (bits == 8) {
+    if (w_bf16) TP_UNROT(8, uint16_t); else TP_UNROT(8, float);
+  } else {
+    if (w_bf16) TP_UNROT(4, uint16_t); else TP_UNROT(4, float);
+  }
+#undef TP_UNROT
+  return hipGetLastError();
+}
+
+hipError_t launch_requantize(const void* q_in, int bits_in, int64_t ldq_in, const float* s_in, int64_t n, int64_t k,
+                             int bits_out, void* q_out, int64_t ldq_out, float* s_out, hipStream_t stream) {
+  const int groups = (int)(k / 256);
+  const dim3 grid((unsigned)((n + 3) / 4)), block(256);
+#define TP_REQ(B, MODE)                                                                                        \
+  hipLaunchKernelGGL((k_rotq_rows<DequantSrc<B>, MODE>), grid, block, 0, stream,                                 \
+                     DequantSrc<B>{(const uint8_t*)q_in, ldq_in, s_in, groups}, n, groups, 0, (uint8_t*)q_out,   \
+                     ldq_out, s_out)
+  if (bits_in == 8) {
+    if (bits_out == 8) TP_REQ(8, MODE_I8_ROW); else TP_REQ(8, MODE_I4_GROUP);
+  } else {
+    if (bits_out == 8) TP_REQ(4, MODE_I8_ROW); else TP_REQ(4, MODE_I4_GROUP);
+  }
+#undef TP_REQ
   return hipGetLastError();
 }
 

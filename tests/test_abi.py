@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.tp_abi_version() == 4
+    assert lib.tp_abi_version() == 5
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.tp_status_string(code).decode() == name
 
@@ -258,6 +258,55 @@ def test_prequantized_refusals(lib, kw, status):
 def test_prequantized_large_m_needs_no_workspace(lib):
     assert lib.tp_workspace_size(4, 4096, 9216, 3072, 0) == 0
     assert pq(lib, m=0, ws=0, wsb=0) == 0
+
+
+# -------------------------------------------------------------- loader
+def du(lib, q=A, bits=8, ldq=512, s=C, n=64, k=512, w=D, wd=0, ldw=512):
+    return lib.tp_dequantize_unrotate(q, bits, ldq, s, n, k, w, wd, ldw, None)
+
+
+def rq8(lib, qi=A, bi=8, ldi=512, si=C, n=64, k=512, bo=4, qo=D, ldo=256, so=E):
+    return lib.tp_requantize_weights(qi, bi, ldi, si, n, k, bo, qo, ldo, so, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=300, ldq=304, ldw=304), 3),
+    (dict(n=-1), 2),
+    (dict(q=0), 1),
+    (dict(s=0), 1),
+    (dict(w=0), 1),
+    (dict(bits=2), 7),
+    (dict(bits=4, ldq=200), 4),
+    (dict(ldw=500), 4),
+    (dict(wd=4), 6),
+    (dict(w=A + 1024), 10),
+    (dict(s=C + 2), 5),
+    (dict(ldw=2 ** 61), 8),
+])
+def test_dequantize_unrotate_refusals(lib, kw, status):
+    assert du(lib, **kw) == status, _err(lib)
+    assert _err(lib)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=300, ldi=304, ldo=304), 3),
+    (dict(qi=0), 1),
+    (dict(so=0), 1),
+    (dict(bi=5), 7),
+    (dict(bo=16), 7),
+    (dict(ldo=200), 4),                # int4 rows are k/2 = 256 bytes
+    (dict(bo=8, ldo=256), 4),          # int8 rows are k bytes
+    (dict(qo=A + 64), 10),             # q_out overlaps q_in
+    (dict(so=D + 128), 10),            # s_out overlaps q_out
+])
+def test_requantize_refusals(lib, kw, status):
+    assert rq8(lib, **kw) == status, _err(lib)
+    assert _err(lib)
+
+
+def test_loader_empty_is_noop(lib):
+    assert du(lib, n=0) == 0
+    assert rq8(lib, n=0) == 0
 
 
 # ---------------------------------------------------------------- W4A8
