@@ -53,6 +53,8 @@ the design notes):
       (Q is its own inverse), exact in fp64 (oracle/loader.py).
   R20 Requantizing to another width is quantizing q * s in the rotated
       domain (rotation after un-rotation is the identity).
+  R21 LoRA side path: c + alpha * (x . A^T) . B^T with lora_A [r, K] and
+      lora_B [N, r] (oracle/lora.py).
   R18 W4A8: the 4-bit weights (one scale per row and 256-group) against the
       per-row int8 activations of R9: exact integer sums per group, then
       y = sa[m] * sum_g s[n, g] * acc_g.
@@ -75,6 +77,7 @@ from .quantize import (
 from .products import qgemm_w8, qgemm_w4, qgemm_w8a8, qgemm_w4a8, int_accumulate, group_accumulate
 from .ffn import silu_mul, swiglu_bf16, ffn_middle_int8, ffn_middle_rotated
 from .loader import dequantize, dequantize_unrotate, requantize
+from .lora import lora_delta, lora_add
 
 __all__ = [
     "GROUP",
@@ -88,6 +91,8 @@ __all__ = [
     "unpack_int4",
     "dequantize_int8",
     "dequantize_int4",
+    "lora_delta",
+    "lora_add",
     "dequantize",
     "dequantize_unrotate",
     "requantize",

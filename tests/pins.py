@@ -491,3 +491,41 @@ def check_loader(dequantize_unrotate, requantize, quantize_weights_int8, quantiz
         assert s8c[r] == sr, "int4 -> int8 scale"
         want = [max(-127, min(127, int(np.rint(v / float(sr))))) for v in vals]
         assert list(q8c[r].astype(int)) == want, "int4 -> int8 codes"
+
+
+# -------------------------------------------------------------------- LoRA
+def check_lora(lora_add, rotate_groups, seed=27):
+    """The side path c + alpha (x A^T) B^T (reading R21).
+
+    * pure-Python loops on a tiny case;
+    * rank one with unit vectors: A = e_i, B = e_j adds alpha x[:, i] to
+      column j only;
+    * alpha = 0 leaves c unchanged, and the result is linear in alpha;
+    * rotating x and A alike leaves it unchanged.
+    """
+    rng = np.random.default_rng(seed)
+    m, n, k, r = 3, 5, 256, 4
+    x = rng.standard_normal((m, k))
+    a = rng.standard_normal((r, k))
+    b = rng.standard_normal((n, r))
+    c = rng.standard_normal((m, n))
+    y = lora_add(c, x, a, b, 0.75)
+    for i in range(m):
+        for j in range(n):
+            t = [sum(x[i, kk] * a[jj, kk] for kk in range(k)) for jj in range(r)]
+            want = c[i, j] + 0.75 * sum(t[jj] * b[j, jj] for jj in range(r))
+            assert abs(y[i, j] - want) <= 1e-12 * (1 + abs(want)), "side path loops"
+    e_a = np.zeros((1, k))
+    e_a[0, 17] = 1.0
+    e_b = np.zeros((n, 1))
+    e_b[2, 0] = 1.0
+    y1 = lora_add(c, x, e_a, e_b, 2.0)
+    want = c.copy()
+    want[:, 2] += 2.0 * x[:, 17]
+    assert np.array_equal(y1, want), "rank one with unit vectors"
+    assert np.array_equal(lora_add(c, x, a, b, 0.0), c), "alpha = 0"
+    d1 = lora_add(c, x, a, b, 1.0) - c
+    d3 = lora_add(c, x, a, b, 3.0) - c
+    assert np.allclose(d3, 3.0 * d1, rtol=1e-13, atol=1e-13), "linear in alpha"
+    y2 = lora_add(c, rotate_groups(x), rotate_groups(a), b, 0.75)
+    assert np.allclose(y2, y, rtol=1e-12, atol=1e-12), "rotation invariance"

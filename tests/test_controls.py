@@ -231,3 +231,14 @@ def test_requantize_int4_scale_index_caught():
         return oracle.requantize(q, s, bits_in, bits_out)
     with pytest.raises(AssertionError):
         pins.check_loader(oracle.dequantize_unrotate, req, *_loader_args())
+
+
+# ------------------------------------------------------------------ LoRA
+@pytest.mark.parametrize("bad", [
+    lambda c, x, a, b, al: np.asarray(c) + al * (np.asarray(x) @ np.asarray(a).T) @ np.asarray(b),   # B not transposed
+    lambda c, x, a, b, al: np.asarray(c) + (np.asarray(x) @ np.asarray(a).T) @ np.asarray(b).T,       # strength dropped
+    lambda c, x, a, b, al: al * (np.asarray(x) @ np.asarray(a).T) @ np.asarray(b).T,                  # output replaced
+])
+def test_lora_faults_caught(bad):
+    with pytest.raises((AssertionError, ValueError)):
+        pins.check_lora(bad, oracle.rotate_groups)

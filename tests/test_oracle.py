@@ -92,3 +92,7 @@ def test_w4a8():
 def test_loader():
     pins.check_loader(oracle.dequantize_unrotate, oracle.requantize, oracle.quantize_weights_int8,
                       oracle.quantize_weights_int4, oracle.pack_int4, oracle.hadamard_matrix)
+
+
+def test_lora():
+    pins.check_lora(oracle.lora_add, oracle.rotate_groups)
