@@ -363,6 +363,44 @@ def next_rows(args, cpu):
             row["cpu_baseline"] = {"value": round(alg * rows / wl.n / dt / 1e9, 3), "unit": "GB/s", "kind": "oracle",
                                    "sample": f"first {rows} weight rows, median of 3 ({dt:.2f} s)"}
         res.append(row)
+    del q8, s8, wh, q4, s4
+
+    # NEXT-4: a LoRA side path (rank 32 and 64) added into the W8A8 qkv
+    # projection's fp32 output, against the product's own time.
+    wl = W.DIT_QKV
+    x, w = W.generate(wl)
+    xd = x.to(d)
+    q8, s8 = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    y = tp.tp_qgemm_w8a8(xd, q8, s8)
+    prod_us = _time_us(torch, lambda: tp.tp_qgemm_w8a8(xd, q8, s8, out=y))
+    for r in (32, 64):
+        a = (torch.randn((r, wl.k), device=d) * 0.02).to(torch.bfloat16)
+        b = (torch.randn((wl.n, r), device=d) * 0.02).to(torch.bfloat16)
+        wsl = torch.empty((tp.tp_lora_workspace_size(wl.m, r),), dtype=torch.uint8, device=d)
+        us = _time_us(torch, lambda: tp.tp_lora_add(y, xd, a, b, 0.8, workspace=wsl))
+        alg = wl.m * wl.k * 2 + r * wl.k * 2 + wl.n * r * 2 + 2 * wl.m * wl.n * 4 + 2 * wl.m * r * 4
+        row = {"row": "lora", "workload": f"rank {r} beside dit_qkv: M={wl.m}, K={wl.k}, N={wl.n}, bf16 x/A/B, fp32 C",
+               "us": round(us, 2), "roofline": {"bound": "hbm", "achieved": round(alg / us / 1e3, 1),
+                                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                                "frac": round(alg / us / 1e3 / PEAK_HBM_GBS, 4),
+                                                "algorithmic_bytes": int(alg)},
+               "vs_product": f"{us / prod_us * 100:.1f}% of the W8A8 qkv product ({prod_us:.1f} us incl. its "
+                             f"activation quantization)"}
+        if cpu:
+            import oracle
+            rows = 64
+            x64 = x[:rows].double().numpy()
+            a64, b64 = a.double().cpu().numpy(), b.double().cpu().numpy()
+            c64 = np.zeros((rows, wl.n))
+            times = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.lora_add(c64, x64, a64, b64, 0.8)
+                times.append(time.perf_counter() - t0)
+            dt = float(np.median(times))
+            row["cpu_baseline"] = {"value": round(alg * rows / wl.m / dt / 1e9, 3), "unit": "GB/s", "kind": "oracle",
+                                   "sample": f"first {rows} rows, median of 3 ({dt:.3f} s)"}
+        res.append(row)
     return res
 
 

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 5
+#define TP_ABI_VERSION 6
 
 typedef enum tp_status {
   TP_OK = 0,
@@ -180,6 +180,33 @@ tp_status tp_dequantize_unrotate(const void* q, int bits, int64_t ldq_bytes, con
 tp_status tp_requantize_weights(const void* q_in, int bits_in, int64_t ldq_in, const float* s_in,
                                 int64_t n, int64_t k, int bits_out, void* q_out, int64_t ldq_out,
                                 float* s_out, hipStream_t stream);
+
+/*
+ * tp_lora_add -- a LoRA side path beside a projection, added into its output
+ * (kvad-gpu internals, section "Pictures, which are not tokens": each LoRA is
+ * a side path (x.A).B beside the layer it adapts, with a per-request strength;
+ * the loaded, quantized weights stay as they are):
+ *
+ *   C[i, j] += alpha * sum_t (sum_q X[i, q] * lora_a[t, q]) * lora_b[j, t]
+ *
+ *   x        [m, k] (TP_F32 or TP_BF16), row pitch ldx: the activations in the
+ *            domain of lora_a (pass the un-rotated activations, or rotate
+ *            lora_a with tp_hadamard_rotate_rows as well: (xQ)(AQ)^T = xA^T).
+ *   lora_a   [r, k], lora_b [n, r], both ab_dtype, row pitches lda, ldb
+ *            (elements; 16-byte aligned rows, as for every matrix operand, so
+ *            lora_b rows are padded to 8 bf16 or 4 fp32); 1 <= r <= 64.
+ *   c        [m, n] (TP_F32 or TP_BF16), row pitch ldc: read, added to,
+ *            written back (rounded once).
+ *   workspace  tp_lora_workspace_size(m, r) bytes (fp32 x . lora_a^T in rows
+ *            of 64), 16-byte aligned.
+ *   Arithmetic is fp32 (inputs widened exactly), summed in a fixed order.
+ *   k must be a multiple of 256, as for the projection.
+ */
+size_t tp_lora_workspace_size(int64_t m, int64_t r);
+tp_status tp_lora_add(const void* x, tp_dtype x_dtype, int64_t ldx, const void* lora_a,
+                      const void* lora_b, tp_dtype ab_dtype, int64_t lda, int64_t ldb, float alpha,
+                      int64_t m, int64_t n, int64_t k, int64_t r, void* c, tp_dtype c_dtype,
+                      int64_t ldc, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* out_kind of tp_swiglu_rotate. */
 #define TP_FFN_OUT_I8 0   /* int8 codes [m, k] and fp32 scales [m] */

@@ -306,3 +306,30 @@ def tp_requantize_weights(q, scales, bits_in, bits_out, q_out=None, scales_out=N
     _lib.check(_lib.load().tp_requantize_weights(q.data_ptr(), bits_in, ldq, scales.data_ptr(), n, k, bits_out,
                                                  q_out.data_ptr(), ldo, scales_out.data_ptr(), _stream(stream)))
     return q_out, scales_out
+
+
+def tp_lora_workspace_size(m, r):
+    """Bytes of workspace tp_lora_add needs for m rows at rank r."""
+    return int(_lib.load().tp_lora_workspace_size(m, r))
+
+
+def tp_lora_add(c, x, lora_a, lora_b, alpha, workspace=None, stream=None):
+    """c += alpha * (x . lora_a^T) . lora_b^T in place (lora_a [r, k],
+    lora_b [n, r], same dtype; r <= 64). Returns c."""
+    ldx = _mat(x, "x")
+    m, k = x.shape
+    r = lora_a.shape[0]
+    n = c.shape[1]
+    if lora_a.shape[1] != k or lora_b.shape != (n, r) or c.shape[0] != m or lora_a.dtype != lora_b.dtype:
+        raise ValueError("shapes/dtypes: x [m, k], lora_a [r, k], lora_b [n, r] (same dtype), c [m, n]")
+    lda = _mat(lora_a, "lora_a")
+    ldb = _mat(lora_b, "lora_b")
+    ldc = _mat(c, "c")
+    need = _lib.load().tp_lora_workspace_size(m, r)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=x.device)
+    _lib.check(_lib.load().tp_lora_add(x.data_ptr(), _dt(x), ldx, lora_a.data_ptr(), lora_b.data_ptr(), _dt(lora_a),
+                                       lda, ldb, float(alpha), m, n, k, r, c.data_ptr(), _dt(c), ldc,
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream(stream)))
+    return c

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtp.so")
-SOURCES = ["api.cpp", "rotate.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "rotate.hip", "gemm.hip", "lora.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

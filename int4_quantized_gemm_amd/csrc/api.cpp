@@ -277,6 +277,45 @@ tp_status check_codes(const char* name, const void* q, int bits, int64_t n, int6
 
 }  // namespace
 
+size_t tp_lora_workspace_size(int64_t m, int64_t r) {
+  if (m < 0 || r < 1 || r > 64 || m > INT_MAX) return 0;
+  return (size_t)(m * 64 * 4);  // fp32 rows of 64 (zeros past r)
+}
+
+tp_status tp_lora_add(const void* x, tp_dtype x_dtype, int64_t ldx, const void* lora_a, const void* lora_b,
+                      tp_dtype ab_dtype, int64_t lda, int64_t ldb, float alpha, int64_t m, int64_t n, int64_t k,
+                      int64_t r, void* c, tp_dtype c_dtype, int64_t ldc, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (!dtype_ok(x_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "x_dtype %d is not TP_F32 or TP_BF16", (int)x_dtype);
+  if (!dtype_ok(ab_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "ab_dtype %d is not TP_F32 or TP_BF16", (int)ab_dtype);
+  if (!dtype_ok(c_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "c_dtype %d is not TP_F32 or TP_BF16", (int)c_dtype);
+  TP_TRY(check_sizes(m, n, k));
+  if (r < 1 || r > 64) return fail(TP_ERR_BAD_SHAPE, "rank r=%lld outside [1, 64]", (long long)r);
+  const int64_t ex = dtype_size(x_dtype), eab = dtype_size(ab_dtype), ec_ = dtype_size(c_dtype);
+  Extent e_x, e_a, e_b, e_c, e_w;
+  TP_TRY(check_matrix("x", x, m, k * ex, ldx, ex, &e_x));
+  TP_TRY(check_matrix("lora_a", lora_a, r, k * eab, lda, eab, &e_a));
+  TP_TRY(check_matrix("lora_b", lora_b, n, r * eab, ldb, eab, &e_b));
+  TP_TRY(check_matrix("c", c, m, n * ec_, ldc, ec_, &e_c, ec_));
+  const int64_t need = m * 64 * 4;
+  if (m > 0 && n > 0) {
+    if (!workspace || (int64_t)workspace_bytes < need)
+      return fail(TP_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %lld needed (tp_lora_workspace_size)",
+                  workspace_bytes, (long long)need);
+    if (((uintptr_t)workspace & 15u) != 0) return fail(TP_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    e_w.lo = (uintptr_t)workspace;
+    e_w.hi = e_w.lo + (uintptr_t)need;
+  }
+  const Extent* ins[] = {&e_x, &e_a, &e_b};
+  for (const Extent* i : ins)
+    if (overlaps(e_c, *i) || overlaps(e_w, *i)) return fail(TP_ERR_BAD_ALIASING, "c or the workspace overlaps an input");
+  if (overlaps(e_c, e_w)) return fail(TP_ERR_BAD_ALIASING, "c and the workspace overlap");
+  if (m == 0 || n == 0) return ok();
+  return hip_status(tp::launch_lora_add(x, x_dtype == TP_BF16, ldx, lora_a, lora_b, ab_dtype == TP_BF16, lda, ldb,
+                                        alpha, m, n, k, r, c, c_dtype == TP_BF16, ldc, (float*)workspace, stream),
+                    "lora launch");
+}
+
 tp_status tp_dequantize_unrotate(const void* q, int bits, int64_t ldq_bytes, const float* scales, int64_t n,
                                  int64_t k, void* w, tp_dtype w_dtype, int64_t ldw, hipStream_t stream) {
   if (!dtype_ok(w_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "w_dtype %d is not TP_F32 or TP_BF16", (int)w_dtype);

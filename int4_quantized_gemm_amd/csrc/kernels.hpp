@@ -24,6 +24,12 @@ hipError_t launch_dequant_unrotate(const void* q, int bits, int64_t ldq, const f
 hipError_t launch_requantize(const void* q_in, int bits_in, int64_t ldq_in, const float* s_in, int64_t n, int64_t k,
                              int bits_out, void* q_out, int64_t ldq_out, float* s_out, hipStream_t stream);
 
+// LoRA side path: c += alpha * (x . a^T) . b^T with a [r, k], b [n, r]
+// (r <= 64); t is fp32 [m, r] scratch.
+hipError_t launch_lora_add(const void* x, bool x_bf16, int64_t ldx, const void* a, const void* b, bool ab_bf16,
+                           int64_t lda, int64_t ldb, float alpha, int64_t m, int64_t n, int64_t k, int64_t r, void* c,
+                           bool c_bf16, int64_t ldc, float* t, hipStream_t stream);
+
 // FFN middle: h = bf16(silu(g) * u), rotated per 256-group, then int8 codes
 // with one scale per row (out_i8) or bf16 rows (scales unused).
 hipError_t launch_swiglu_rotate(const void* g, int64_t ldg, const void* u, int64_t ldu, bool in_bf16, int64_t m,

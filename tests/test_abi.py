@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.tp_abi_version() == 5
+    assert lib.tp_abi_version() == 6
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.tp_status_string(code).decode() == name
 
@@ -258,6 +258,44 @@ def test_prequantized_refusals(lib, kw, status):
 def test_prequantized_large_m_needs_no_workspace(lib):
     assert lib.tp_workspace_size(4, 4096, 9216, 3072, 0) == 0
     assert pq(lib, m=0, ws=0, wsb=0) == 0
+
+
+# ---------------------------------------------------------------- LoRA
+def lo(lib, x=A, xd=1, ldx=512, la=B, lb=B + 65536, abd=1, lda=512, ldb=32, alpha=0.5, m=64, n=256, k=512, r=32,
+       c=D, cd=0, ldc=256, ws=E, wsb=1 << 20):
+    return lib.tp_lora_add(x, xd, ldx, la, lb, abd, lda, ldb, alpha, m, n, k, r, c, cd, ldc, ws or None, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=300, ldx=304, lda=304), 3),
+    (dict(r=0), 2),
+    (dict(r=65, ldb=65), 2),
+    (dict(x=0), 1),
+    (dict(la=0), 1),
+    (dict(c=0), 1),
+    (dict(ldb=16), 4),
+    (dict(ldx=500), 4),
+    (dict(x=A + 1), 5),
+    (dict(xd=2), 6),
+    (dict(abd=9), 6),
+    (dict(cd=5), 6),
+    (dict(ws=0, wsb=0), 9),
+    (dict(wsb=64 * 64 * 4 - 4), 9),
+    (dict(ldb=33), 5),                 # lora_b rows must be 16-byte aligned
+    (dict(ws=E + 8), 5),
+    (dict(c=A + 256), 10),             # c overlaps x
+    (dict(ws=D + 64), 10),             # workspace overlaps c
+])
+def test_lora_refusals(lib, kw, status):
+    assert lo(lib, **kw) == status, _err(lib)
+    assert _err(lib)
+
+
+def test_lora_workspace_and_empty(lib):
+    assert lib.tp_lora_workspace_size(4096, 32) == 4096 * 64 * 4
+    assert lib.tp_lora_workspace_size(4096, 65) == 0
+    assert lo(lib, m=0, ws=0, wsb=0) == 0
+    assert lo(lib, n=0, ws=0, wsb=0) == 0
 
 
 # -------------------------------------------------------------- loader
