@@ -158,7 +158,8 @@ struct PPCfg {
 // fp32 for W4 and W4A8, the latter before the activation scale) to part[blockIdx.y][m][n] instead of C; k_qgemm_reduce adds the
 // splits in order and applies the epilogue. sps is a multiple of 4 (whole
 // 256-groups).
-template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE, bool OUT_BF16, bool ACC_OUT, bool PARTIAL>
+template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE, bool OUT_BF16, bool ACC_OUT, bool PARTIAL,
+          bool EWD = false>
 __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
     const uint8_t* __restrict__ A, int64_t lda_bytes, const uint8_t* __restrict__ B, int64_t ldb_bytes,
     const float* __restrict__ sw, const float* __restrict__ sa, int M, int N, int K, void* __restrict__ Cv,
@@ -259,6 +260,12 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   u32x4_t fa[NKK][FM];
   typedef typename std::conditional<Cfg::B4, uint2, u32x4_t>::type braw_t;
   braw_t fb[FN];
+  // EWD (W8, W4): the weight fragments are widened at the end of the memory
+  // phase, where this wave's VALU work runs beside the other group's MFMAs,
+  // instead of in the compute phase, where it would serialize with this
+  // wave's own.
+  constexpr bool EW = EWD && (KIND == GEMM_W8 || KIND == GEMM_W4);
+  bf16x8_t wb[EW ? FN : 1][2];
   float s_nx[KIND == GEMM_W4 ? FN : 1];  // W4: scales of the next group
   float s_grp[KIND == GEMM_W4A8 ? FN : 1];  // W4A8: scales of the group being folded
 
@@ -320,6 +327,19 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
       }
     }
     if (ks + NSTAGE - 1 < KS) issue_stage(ks + NSTAGE - 1);
+    if constexpr (EW) {
+      __builtin_amdgcn_s_waitcnt(LGKMCNT0_ENCODE);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (KIND == GEMM_W4) {
+          wb[j][0] = pp_widen_i4x8_x16(fb[j].x, mk[j]);
+          wb[j][1] = pp_widen_i4x8_x16(fb[j].y, mk[j]);
+        } else {
+          wb[j][0] = pp_widen_i8x8(fb[j].x, fb[j].y);
+          wb[j][1] = pp_widen_i8x8(fb[j].z, fb[j].w);
+        }
+      }
+    }
   };
 
   auto compute_phase = [&](int ks) {
@@ -354,6 +374,18 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int i = 0; i < FM; ++i) tot[i][j] += s_grp[j] * __builtin_convertvector(acc[i][j], f32x4_t);
+      }
+    } else if constexpr (EW) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[0][i]), wb[j][0],
+                                                               acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[1][i]), wb[j][1],
+                                                               acc[i][j], 0, 0, 0);
       }
     } else {
       // W8: the widening of fragment j+1 is interleaved with the MFMAs of
@@ -571,7 +603,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
 
 // splits > 1: K split over blockIdx.y into ranges of sps stages, partial sums
 // in g.part, then k_qgemm_reduce (gemm_skinny.hpp).
-template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE>
+template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE, bool EWD = false>
 static hipError_t launch_pp(const GemmArgs& g, hipStream_t stream, int gm = 8, int splits = 1, int sps = 0) {
   const int tiles_m = (int)((g.m + BM - 1) / BM), tiles_n = (int)((g.n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(512);
@@ -579,7 +611,7 @@ static hipError_t launch_pp(const GemmArgs& g, hipStream_t stream, int gm = 8, i
   const uint8_t* a = (const uint8_t*)g.a;
   const uint8_t* b = (const uint8_t*)g.b;
 #define TP_LAUNCH_PP(OB, AO, PA)                                                                                  \
-  hipLaunchKernelGGL((k_qgemm_pp<KIND, BM, BN, WM, WN, NSTAGE, OB, AO, PA>), grid, block, 0, stream, a, lda_bytes, b, \
+  hipLaunchKernelGGL((k_qgemm_pp<KIND, BM, BN, WM, WN, NSTAGE, OB, AO, PA, EWD>), grid, block, 0, stream, a, lda_bytes, b, \
                      g.ldb, g.w_scales, g.a_scales, (int)g.m, (int)g.n, (int)g.k, g.c, g.ldc, g.acc_out, g.ld_acc,    \
                      tiles_m, tiles_n, gm, sps, g.part)
   if (splits > 1) {
