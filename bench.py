@@ -71,16 +71,21 @@ def step_plan():
             ("w8", W.FFN_UP), ("w4", W.FFN_DOWN)]
 
 
+# The sources of the product kernels (the translation unit gemm.hip and what
+# it includes): the counter profile of a product applies only while they are
+# unchanged.
+GEMM_SOURCES = ("gemm.hip", "gemm_pp.hpp", "gemm_skinny.hpp", "device_common.hpp", "kernels.hpp")
+
+
 def _src_hash():
-    """Hash of every kernel source: a committed counter profile applies only
-    to the kernels it was taken on."""
+    """Hash of the product kernels' sources: a committed counter profile
+    applies only to the kernels it was taken on."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "int4_quantized_gemm_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(f.encode())
-                h.update(fh.read())
+    for f in GEMM_SOURCES:
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
