@@ -33,9 +33,10 @@ namespace tp {
 //          in the memory phase (EWD; 3-5% faster than in the compute phase,
 //          where a wave's VALU work serializes with its own MFMAs; slower for
 //          W4, whose memory phase is the longer one);
-//   W8A8   256x256 (128x64 waves), 4 stages; 256x192 (64x96 waves) when the
-//          256x256 grid would leave CUs idle and the 192-wide one does not
-//          (e.g. N = 3072 at M = 4096: 192 -> 256 tiles for 256 CUs);
+//   W8A8   256x256 (128x64 waves), 4 stages, or 256x192 (64x96 waves) when
+//          its rounds of tiles, at 0.825 of a 256x256 tile's time each, take
+//          less (N = 3072 at M = 4096: one full round of 256 tiles instead of
+//          192 tiles; N = 9216: 3 full rounds instead of 2.25);
 //   W4     256x192 (128x48 waves), 3 stages, when that grid has at least 192
 //          tiles (4032x3072 splits into exactly 256): 128-row waves spread
 //          the widening of each code over 8 MFMAs (measured 4032x3072x12288:
@@ -70,8 +71,15 @@ static PpPlan pick_plan(int kind, int64_t m, int64_t n, int64_t k) {
     return PpPlan{CFG_PP_256x128, 1, 0};
   if (big >= 128) {
     if (kind == GEMM_W4 || kind == GEMM_W4A8) return PpPlan{CFG_PP_128x192, 1, 0};
-    if (kind == GEMM_W8A8 && big < NUM_CUS && ((m + 255) / 256) * ((n + 191) / 192) <= NUM_CUS)
-      return PpPlan{CFG_PP_256x192, 1, 0};
+    if (kind == GEMM_W8A8) {
+      // Rounds of tiles on the CUs, weighted by a tile's time: a 256x192 tile
+      // (64x96 waves) takes about 0.825 of a 256x256 one (0.75 of the area at
+      // a lower rate). 4096x9216: 3 rounds of 256x256 (the last a quarter
+      // full) against 3 of 256x192, 131 -> 119 us.
+      const int64_t r256 = (big + NUM_CUS - 1) / NUM_CUS;
+      const int64_t r192 = (((m + 255) / 256) * ((n + 191) / 192) + NUM_CUS - 1) / NUM_CUS;
+      if (r192 * 33 < r256 * 40) return PpPlan{CFG_PP_256x192, 1, 0};
+    }
     return PpPlan{CFG_PP_256x256, 1, 0};
   }
   const int64_t tiles = ((m + 127) / 128) * ((n + 191) / 192);
