@@ -29,10 +29,10 @@ namespace tp {
 
 // Kernel table (from measured sweeps on MI355X). Outputs with at least 128
 // tiles of 256x256 run the two-group multi-stage kernel of gemm_pp.hpp:
-//   W8     256x256 tiles of 8 waves (128x64 each), 3 stages, codes widened
-//          in the memory phase (EWD; 3-5% faster than in the compute phase,
-//          where a wave's VALU work serializes with its own MFMAs; slower for
-//          W4, whose memory phase is the longer one);
+//   W8     256x256 tiles of 8 waves (128x64 each), 3 stages, all four code
+//          fragments widened in the memory phase (3-5% faster than in the
+//          compute phase, where a wave's VALU work serializes with its own
+//          MFMAs);
 //   W8A8   256x256 (128x64 waves), 4 stages, or 256x192 (64x96 waves) when
 //          its rounds of tiles, at 0.825 of a 256x256 tile's time each, take
 //          less (N = 3072 at M = 4096: one full round of 256 tiles instead of
@@ -40,7 +40,10 @@ namespace tp {
 //   W4     256x192 (128x48 waves), 3 stages, when that grid has at least 192
 //          tiles (4032x3072 splits into exactly 256): 128-row waves spread
 //          the widening of each code over 8 MFMAs (measured 4032x3072x12288:
-//          391 us with 64x48 waves and a second accumulator set, 277 us);
+//          391 us with 64x48 waves and a second accumulator set, 277 us),
+//          two of the three code fragments widened in the memory phase and
+//          one in the compute phase (6% faster than none or all early: the
+//          phases balance, measured with per-phase timestamps);
 //          below that, 128x192 (64x48 waves, 5 stages);
 //   W4A8   256x128 (128x32 waves, 5 stages) when that grid fills the CUs at
 //          least twice (the per-group fold keeps a second accumulator set,
@@ -136,11 +139,11 @@ static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
     case CFG_PP_256x256:
       if constexpr (KIND == GEMM_W8A8)
         return launch_pp<KIND, 256, 256, 128, 64, 4>(g, stream, (g.n + 255) / 256 >= 64 ? 4 : 8);
-      if constexpr (KIND == GEMM_W8) return launch_pp<KIND, 256, 256, 128, 64, 3, true>(g, stream, 4);
+      if constexpr (KIND == GEMM_W8) return launch_pp<KIND, 256, 256, 128, 64, 3, 4>(g, stream, 4);
       break;
     case CFG_PP_256x192:
       if constexpr (KIND == GEMM_W8A8) return launch_pp<KIND, 256, 192, 64, 96, 4>(g, stream);
-      if constexpr (KIND == GEMM_W4) return launch_pp<KIND, 256, 192, 128, 48, 3>(g, stream, 4);
+      if constexpr (KIND == GEMM_W4) return launch_pp<KIND, 256, 192, 128, 48, 3, 2>(g, stream, 4);
       break;
     case CFG_PP_256x128:
       if constexpr (KIND == GEMM_W4A8) return launch_pp<KIND, 256, 128, 128, 32, 5>(g, stream, 4);
