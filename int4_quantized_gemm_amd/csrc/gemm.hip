@@ -29,10 +29,10 @@ namespace tp {
 
 // Kernel table (from measured sweeps on MI355X). Outputs with at least 128
 // tiles of 256x256 run the two-group multi-stage kernel of gemm_pp.hpp:
-//   W8     256x256 tiles of 8 waves (128x64 each), 3 stages, all four code
-//          fragments widened in the memory phase (3-5% faster than in the
-//          compute phase, where a wave's VALU work serializes with its own
-//          MFMAs);
+//   W8     256x256 tiles of 8 waves (128x64 each), 3 stages, three of the
+//          four code fragments widened in the memory phase (5-7% faster than
+//          all in the compute phase, where a wave's VALU work serializes with
+//          its own MFMAs; 1.7% faster than all four early);
 //   W8A8   256x256 (128x64 waves), 4 stages, or 256x192 (64x96 waves) when
 //          its rounds of tiles, at 0.825 of a 256x256 tile's time each, take
 //          less (N = 3072 at M = 4096: one full round of 256 tiles instead of
@@ -139,7 +139,7 @@ static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
     case CFG_PP_256x256:
       if constexpr (KIND == GEMM_W8A8)
         return launch_pp<KIND, 256, 256, 128, 64, 4>(g, stream, (g.n + 255) / 256 >= 64 ? 4 : 8);
-      if constexpr (KIND == GEMM_W8) return launch_pp<KIND, 256, 256, 128, 64, 3, 4>(g, stream, 4);
+      if constexpr (KIND == GEMM_W8) return launch_pp<KIND, 256, 256, 128, 64, 3, 3>(g, stream, 4);
       break;
     case CFG_PP_256x192:
       if constexpr (KIND == GEMM_W8A8) return launch_pp<KIND, 256, 192, 64, 96, 4>(g, stream);

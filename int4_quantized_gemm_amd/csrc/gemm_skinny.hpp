@@ -43,6 +43,10 @@ struct SkTraits {
   static constexpr int LPG = WBG / 64;                     // 16-byte loads per lane per fragment per group
 };
 
+// Column XOR of activation row r (0-15) in LDS: r with bit 3 flipped when
+// bit 2 is set (see the activation staging in k_qgemm_skinny).
+__device__ __forceinline__ int sk_swz(int r) { return r ^ ((r << 1) & 8); }
+
 constexpr int SK_FNW = 2;               // 16-row weight fragments per wave
 constexpr int SK_BN = 4 * 16 * SK_FNW;  // weight rows per block (four waves)
 constexpr int SK_DG = 2;                // 256-groups of codes in flight per wave
@@ -97,8 +101,14 @@ __global__ __launch_bounds__(256) void k_qgemm_skinny(const uint8_t* __restrict_
   // Activation rows m0 .. m0+MR-1 (clamped to M-1: rows past M only feed
   // output rows that are never stored), K range of this split, into LDS with
   // direct-to-LDS loads. LDS slot (row r, 16-byte column c) sits at
-  // r * cpr + (c ^ (r & 15)), so the 16 rows of a fragment read fall in 16
-  // distinct bank groups. Each wave instruction fills 64 consecutive slots.
+  // r * cpr + (c ^ sk_swz(r & 15)). Rows are whole multiples of 256 bytes, so a
+  // slot's bank group is its column modulo 16. A fragment read has lane l
+  // read row l & 15 at a column that grows by 1 (W8A8), 2 (W8) or 4 (W4)
+  // from lane group l >> 4 to the next, and ds_read_b128 serves rows
+  // {0-3, 12-15} of one lane group with rows {4-11} of the next in one pass
+  // (gfx950, measured): sk_swz sends the first set to bank groups 0-7 and the
+  // second to 8-15 for all three steps. Each wave instruction fills 64
+  // consecutive slots.
   const int cpr = ng * 256 * T::AB / 16;  // 16-byte columns per row, a multiple of 16
   {
     const int total = MR * cpr;  // a multiple of 256
@@ -106,7 +116,7 @@ __global__ __launch_bounds__(256) void k_qgemm_skinny(const uint8_t* __restrict_
     const int s = wave * 64 + lane;
     int r = s / cpr, p = s - r * cpr;
     for (int s0 = wave * 64; s0 < total; s0 += 256) {
-      const int c = p ^ (r & 15);
+      const int c = p ^ sk_swz(r & 15);
       const int m = min(m0 + r, M - 1);
       __builtin_amdgcn_global_load_lds((const void*)(abase + (int64_t)m * lda_bytes + c * 16),
                                        (lds_void_t*)(sk_lds + s0 * 16), 16, 0, 0);
@@ -135,7 +145,7 @@ __global__ __launch_bounds__(256) void k_qgemm_skinny(const uint8_t* __restrict_
   const uint8_t* arow = sk_lds + r16 * rowbytes;
   auto afrag = [&](int i, int elem) -> u32x4_t {
     const int c = (elem * T::AB) >> 4;
-    return *reinterpret_cast<const u32x4_t*>(arow + i * 16 * rowbytes + ((c ^ r16) << 4));
+    return *reinterpret_cast<const u32x4_t*>(arow + i * 16 * rowbytes + ((c ^ sk_swz(r16)) << 4));
   };
 
   auto compute_group = [&](const u32x4_t (&w)[SK_FNW][T::LPG], int gi) {
