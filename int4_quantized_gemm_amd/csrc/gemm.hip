@@ -48,7 +48,9 @@ namespace tp {
 //   W4A8   256x128 (128x32 waves, 5 stages) when that grid fills the CUs at
 //          least twice (the per-group fold keeps a second accumulator set,
 //          and 128-row waves halve the widening per MFMA: 4096x12288x3072
-//          286 -> 235 us), else as W4 below 256x192.
+//          286 -> 235 us), else as W4 below 256x192; in both, two code
+//          fragments per stage are widened in the memory phase and the
+//          group fold runs there too (4096x3072x12288: 278 -> 248 us).
 // The last launch argument is the number of tile-rows an XCD walks together
 // (pp_map_tile): 4 for W8, W4 and wide W8A8 outputs, 8 otherwise (measured:
 // W8 4096x3072x12288 307 -> 257 us from 8 to 4).
@@ -146,9 +148,10 @@ static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
       if constexpr (KIND == GEMM_W4) return launch_pp<KIND, 256, 192, 128, 48, 3, 2>(g, stream, 4);
       break;
     case CFG_PP_256x128:
-      if constexpr (KIND == GEMM_W4A8) return launch_pp<KIND, 256, 128, 128, 32, 5>(g, stream, 4);
+      if constexpr (KIND == GEMM_W4A8) return launch_pp<KIND, 256, 128, 128, 32, 5, 2>(g, stream, 4);
       break;
     default:
+      if constexpr (KIND == GEMM_W4A8) return launch_pp<KIND, 128, 192, 64, 48, 5, 2>(g, stream, 4, pl.splits, pl.sps);
       return launch_pp<KIND, 128, 192, 64, 48, 5>(g, stream, 4, pl.splits, pl.sps);
   }
   return hipErrorInvalidValue;

@@ -274,15 +274,27 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   u32x4_t fa[NKK][FM];
   typedef typename std::conditional<Cfg::B4, uint2, u32x4_t>::type braw_t;
   braw_t fb[FN];
-  // Early widening (W8, W4): the first EWF weight fragments are widened at the
-  // end of the memory phase, where this wave's VALU work runs beside the
-  // other group's MFMAs; the rest in the compute phase, where it serializes
-  // with this wave's own. EWN balances the two phases.
-  constexpr int EWF = (KIND == GEMM_W8 || KIND == GEMM_W4) ? (EWN < FN ? EWN : FN) : 0;
-  constexpr bool EW = EWF > 0;
+  // Early widening (W8, W4, W4A8): the first EWF weight fragments are widened
+  // at the end of the memory phase, where this wave's VALU work runs beside
+  // the other group's MFMAs; the rest in the compute phase, where it
+  // serializes with this wave's own. EWN balances the two phases.
+  constexpr int EWF = (KIND == GEMM_W8 || KIND == GEMM_W4 || KIND == GEMM_W4A8) ? (EWN < FN ? EWN : FN) : 0;
+  constexpr bool EW = EWF > 0 && KIND != GEMM_W4A8;
   bf16x8_t wb[EW ? EWF : 1][2];
+  u32x4_t wq[KIND == GEMM_W4A8 && EWF > 0 ? EWF : 1];  // W4A8: int8 (16 * code) fragments
   float s_nx[KIND == GEMM_W4 ? FN : 1];  // W4: scales of the next group
   float s_grp[KIND == GEMM_W4A8 ? FN : 1];  // W4A8: scales of the group being folded
+  // W4A8: fold the int32 sums of the group that just ended into tot, in the
+  // memory phase of the next group's first stage (beside the other group's
+  // MFMAs), and once after the loop.
+  auto fold = [&]() {
+    if constexpr (KIND == GEMM_W4A8) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) tot[i][j] += s_grp[j] * __builtin_convertvector(acc[i][j], f32x4_t);
+    }
+  };
 
   // W4: switch the accumulators to the units of the group whose scales are
   // in s_nx (see cu above).
@@ -303,6 +315,9 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   };
 
   auto mem_phase = [&](int ks) {
+    if constexpr (KIND == GEMM_W4A8) {
+      if ((ks & 3) == 0 && ks > 0) fold();
+    }
     const uint8_t* as = ring + (ks % NSTAGE) * STAGE;
     const uint8_t* bs = as + A_STAGE;
 #pragma unroll
@@ -342,6 +357,10 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
       }
     }
     if (ks + NSTAGE - 1 < KS) issue_stage(ks + NSTAGE - 1);
+    if constexpr (KIND == GEMM_W4A8 && EWF > 0) {
+#pragma unroll
+      for (int j = 0; j < EWF; ++j) wq[j] = pp_widen_i4_i8x16(fb[j]);
+    }
     if constexpr (EW) {
       __builtin_amdgcn_s_waitcnt(LGKMCNT0_ENCODE);
 #pragma unroll
@@ -367,11 +386,16 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
                                                              __builtin_bit_cast(i32x4_t, fb[j]), acc[i][j], 0, 0, 0);
     } else if constexpr (KIND == GEMM_W4A8) {
       // A group's first stage starts its sums from zero (the previous group's
-      // were folded at its last stage).
+      // were folded in this stage's memory phase).
       const bool first = (ks & 3) == 0;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const i32x4_t b = __builtin_bit_cast(i32x4_t, pp_widen_i4_i8x16(fb[j]));
+        u32x4_t bw;
+        if (j < EWF)
+          bw = wq[j];
+        else
+          bw = pp_widen_i4_i8x16(fb[j]);
+        const i32x4_t b = __builtin_bit_cast(i32x4_t, bw);
         if (first) {
 #pragma unroll
           for (int i = 0; i < FM; ++i)
@@ -383,12 +407,6 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
             acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, fa[0][i]), b, acc[i][j],
                                                                0, 0, 0);
         }
-      }
-      if ((ks & 3) == 3) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int i = 0; i < FM; ++i) tot[i][j] += s_grp[j] * __builtin_convertvector(acc[i][j], f32x4_t);
       }
     } else if constexpr (EW) {
 #pragma unroll
@@ -528,6 +546,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
     barrier_only();
   }
   if (grp == 0) barrier_only();
+  fold();
 
   // W4 output of accumulator element (i, j, r): back from units of cu[j]
   // (and from the 16x codes); a column with a skipped group is summed again

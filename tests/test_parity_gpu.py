@@ -375,6 +375,29 @@ def test_w8a8_dit_block_sampled(name):
     _w8a8_case(wl, row_sel=sample_rows(wl.m, 40, seed=wl.seed))
 
 
+@pytest.mark.parametrize("m,n,k", [(4000, 9000, 1024), (4000, 24000, 512)])
+def test_w8a8_large_ragged(m, n, k):
+    """Ragged M and N on the large-tile paths: 4000x9000 takes 256x192 tiles
+    (3 full rounds against 2.25 of 256x256), 4000x24000 256x256 tiles. Sampled
+    rows include the last tile-row's tail."""
+    announce("tp_qgemm_w8a8 large ragged", m, n, k)
+    wl = W.TINY.with_(name=f"ragged{m}x{n}", m=m, n=n, k=k, seed=m + n, act_outliers=3, w_outliers=3, path="w8a8")
+    _w8a8_case(wl, row_sel=sample_rows(m, 24, seed=n))
+
+
+@pytest.mark.parametrize("kind,m,n,k", [("w8", 3000, 5000, 512), ("w4", 4000, 3100, 1024)])
+def test_weight_only_large_ragged(kind, m, n, k):
+    """Ragged M and N on the large-tile paths (W8 256x256, W4 256x192), with
+    the early/late split of the code widening; fp32 output."""
+    announce("tp_qgemm", kind, "large ragged", m, n, k)
+    wl = W.TINY.with_(name=f"ragged{m}x{n}", m=m, n=n, k=k, seed=m + 2 * n, act_outliers=3, w_outliers=3,
+                      path=kind)
+    case = _w8_case if kind == "w8" else _w4_case
+    got, ref = case(wl, row_sel=sample_rows(m, 24, seed=k), out_dtype=torch.float32)
+    err = assert_bf16_path(got, ref, f"{kind} large ragged")
+    assert err < 1e-4
+
+
 @pytest.mark.parametrize("m,n,k", [(1, 256, 256), (100, 200, 768), (129, 385, 512), (257, 131, 1024)])
 def test_w8a8_ragged(m, n, k):
     announce("tp_qgemm_w8a8 ragged", m, n, k)
