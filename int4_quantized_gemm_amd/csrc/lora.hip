@@ -4,13 +4,15 @@
 // the layer it adapts, with a per-request strength, added into the layer's
 // output; the loaded model is left as it was).
 //
-//  * k_lora_down   T[m, j] = sum_k X[m, k] A[j, k]   (fp32 [m, 64], the workspace;
-//                  zeros past r)
-//  * k_lora_up_add C[m, n] += alpha * sum_j T[m, j] B[n, j], read-modify-write
+//  * down  T[m, j] = sum_k X[m, k] A[j, k]   (fp32 [m, 64], the workspace;
+//          zeros past r)
+//  * up    C[m, n] += alpha * sum_j T[m, j] B[n, j], read-modify-write
 //
-// Both run on fp32 FMAs (the side path is 2 r / k of the projection's work):
-// inputs are widened exactly from fp32 or bf16, sums are fp32 in a fixed
-// order, and C is rounded once on store.
+// Sums are fp32 in a fixed order and C is rounded once on store. bf16
+// operands go through the matrix units (k_lora_down_mfma with bf16 X and A,
+// k_lora_up_mfma with bf16 B; every product is exact in fp32), fp32 operands
+// through fp32 FMAs (k_lora_down, k_lora_up_add; inputs widened exactly).
+#include <climits>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -107,11 +109,11 @@ __global__ __launch_bounds__(256) void k_lora_down(const TX* __restrict__ x, int
 template <typename TB, typename TC, int R>
 __global__ __launch_bounds__(256) void k_lora_up_add(const float* __restrict__ t, const TB* __restrict__ b,
                                                      int64_t ldb, float alpha, int M, int N, int r,
-                                                     TC* __restrict__ c, int64_t ldc) {
+                                                     TC* __restrict__ c, int64_t ldc, int nbn) {
   __shared__ __align__(16) float ts[LU_BM][R];
   const int tid = threadIdx.x;
-  const int m0 = blockIdx.y * LU_BM;
-  const int n = blockIdx.x * LU_BN + tid;
+  const int m0 = (int)(blockIdx.x / nbn) * LU_BM;
+  const int n = (int)(blockIdx.x % nbn) * LU_BN + tid;
   for (int e = tid; e < LU_BM * R / 4; e += 256) {
     const int rr = e / (R / 4), j = (e % (R / 4)) * 4;
     *reinterpret_cast<f32x4_t*>(&ts[rr][j]) =
@@ -159,6 +161,194 @@ __global__ __launch_bounds__(256) void k_lora_up_add(const float* __restrict__ t
   }
 }
 
+// ------------------------------------------------------- matrix-unit paths
+// With bf16 operands the products X[m,k] A[j,k] and T-part x B[n,j] are exact
+// in fp32, so bf16 MFMAs with fp32 sums keep the arithmetic above: fp32 sums,
+// C rounded once.
+
+// Down, bf16 X and lora_A: one block per 16 rows of X; its 8 waves split K in
+// eighths (k is a multiple of 256, so each eighth is whole 32-deep steps) and
+// their partial sums are added in LDS in wave order. Lane l feeds X row l % 16
+// and lora_A row 16 f + l % 16 (zero past r) with K chunk 8 (l / 16) of each
+// step.
+template <int R>
+__global__ __launch_bounds__(512) void k_lora_down_mfma(const uint16_t* __restrict__ x, int64_t ldx,
+                                                        const uint16_t* __restrict__ a, int64_t lda, int M, int K,
+                                                        int r, float* __restrict__ t) {
+  constexpr int NF = R / 16;  // 16-column fragments of T
+  __shared__ __align__(16) float part[8][16][R];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int m0 = blockIdx.x * 16;
+  const int kw = K / 8, kb = wave * kw;
+  const bool rowok = m0 + l16 < M;
+  const uint16_t* xrow = x + (int64_t)min(m0 + l16, M - 1) * ldx + kb + 8 * g4;
+  const uint16_t* arow[NF];
+  bool aok[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int j = f * 16 + l16;
+    aok[f] = j < r;
+    arow[f] = a + (int64_t)min(j, r - 1) * lda + kb + 8 * g4;
+  }
+  f32x4_t acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+  for (int k = 0; k < kw; k += 32) {
+    const u32x4_t xv = rowok ? *reinterpret_cast<const u32x4_t*>(xrow + k) : zero;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const u32x4_t av = aok[f] ? *reinterpret_cast<const u32x4_t*>(arow[f] + k) : zero;
+      acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
+                                                       __builtin_bit_cast(bf16x8_t, av), acc[f], 0, 0, 0);
+    }
+  }
+  // lane l holds rows 4 (l / 16) + v, column 16 f + l % 16
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) part[wave][4 * g4 + v][f * 16 + l16] = acc[f][v];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * LORA_RMAX; e += 512) {
+    const int i = e / LORA_RMAX, j = e % LORA_RMAX;
+    if (m0 + i >= M) continue;
+    float sum = 0.f;
+    if (j < R && j < r) {
+      sum = part[0][i][j];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) sum += part[w][i][j];
+    }
+    t[(int64_t)(m0 + i) * LORA_RMAX + j] = sum;
+  }
+}
+
+// fp32 v = hi + mid + lo exactly, each part bf16 (round to nearest even at
+// each step; each residual is exact in fp32 and the last one fits in 8 bits).
+__device__ __forceinline__ void split3_bf16(const float (&v)[8], bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
+  u32x4_t h, m, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a0 = v[2 * e], a1 = v[2 * e + 1];
+    const uint32_t hw = pack_bf16x2(a0, a1);
+    const float r0 = a0 - bf16_lo(hw), r1 = a1 - bf16_hi(hw);
+    const uint32_t mw = pack_bf16x2(r0, r1);
+    const uint32_t lw = pack_bf16x2(r0 - bf16_lo(mw), r1 - bf16_hi(mw));
+    h[e] = hw;
+    m[e] = mw;
+    l[e] = lw;
+  }
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  mid = __builtin_bit_cast(bf16x8_t, m);
+  lo = __builtin_bit_cast(bf16x8_t, l);
+}
+
+// Up, bf16 lora_B: a block owns 16 rows x 256 columns of C, a wave 64 of the
+// columns. T (fp32) is split exactly into three bf16 parts; the two small
+// parts are summed first and the large part last, so the result carries
+// about r + 1 fp32 roundings of sum |T| |B| like the plain fp32 sum. Lane l
+// feeds T row l % 16 and lora_B row n0 + 16 f + l % 16 with ranks
+// 32 s + 8 (l / 16) + [0, 8) (zeros past r; T holds zeros there already).
+// The products go through LDS so that C is read and written a whole row
+// segment (1 KB of fp32) per wave instruction, 16 (fp32) or 8 (bf16) bytes a
+// lane when C's base and pitch allow it (cvec), element by element otherwise.
+constexpr int LUM_PAD = 4;  // floats of padding per LDS row (rows 4 apart land 16 banks apart)
+
+template <typename TC, int R>
+__global__ __launch_bounds__(256) void k_lora_up_mfma(const float* __restrict__ t, const uint16_t* __restrict__ b,
+                                                      int64_t ldb, float alpha, int M, int N, int r,
+                                                      TC* __restrict__ c, int64_t ldc, int nbn, int cvec) {
+  constexpr int KS = (R + 31) / 32;  // 32-deep steps over the rank
+  __shared__ __align__(16) float prod[16][256 + LUM_PAD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int m0 = (int)(blockIdx.x / nbn) * 16;
+  const int nb0 = (int)(blockIdx.x % nbn) * 256;
+  const int n0 = nb0 + wave * 64;
+  bf16x8_t th[KS], tm[KS], tl[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    float v[8];
+    if (m0 + l16 < M) {
+      load8(t + (int64_t)(m0 + l16) * LORA_RMAX + 32 * s + 8 * g4, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    split3_bf16(v, th[s], tm[s], tl[s]);
+  }
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int n = n0 + 16 * f + l16;
+    bf16x8_t bo[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int j0 = 32 * s + 8 * g4;
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (n < N && j0 < r) {
+        const uint16_t* brow = b + (int64_t)n * ldb + j0;
+        if (j0 + 8 <= r) {
+          w = *reinterpret_cast<const u32x4_t*>(brow);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const uint32_t lo = j0 + e < r ? brow[e] : 0u, hi = j0 + e + 1 < r ? brow[e + 1] : 0u;
+            w[e >> 1] = lo | (hi << 16);
+          }
+        }
+      }
+      bo[s] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl[s], bo[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tm[s], bo[s], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th[s], bo[s], acc, 0, 0, 0);
+    // lane l holds rows 4 (l / 16) + v, column 16 f + l % 16 of the wave's 64
+#pragma unroll
+    for (int v = 0; v < 4; ++v) prod[4 * g4 + v][wave * 64 + 16 * f + l16] = acc[v];
+  }
+  __syncthreads();
+  // Read-modify-write of C: thread tid handles 4 columns of row q / 64, q = tid + 256 u.
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = threadIdx.x + 256 * u;
+    const int i = q >> 6, c4 = (q & 63) * 4;
+    const int row = m0 + i, col = nb0 + c4;
+    if (row >= M || col >= N) continue;
+    const f32x4_t pv = *reinterpret_cast<const f32x4_t*>(&prod[i][c4]);
+    TC* p = c + (int64_t)row * ldc + col;
+    if (cvec && col + 4 <= N) {
+      if constexpr (std::is_same<TC, float>::value) {
+        f32x4_t cv = *reinterpret_cast<const f32x4_t*>(p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cv[e] = fmaf(alpha, pv[e], cv[e]);
+        *reinterpret_cast<f32x4_t*>(p) = cv;
+      } else {
+        const uint2 cw = *reinterpret_cast<const uint2*>(p);
+        const float o0 = fmaf(alpha, pv[0], bf16_lo(cw.x)), o1 = fmaf(alpha, pv[1], bf16_hi(cw.x));
+        const float o2 = fmaf(alpha, pv[2], bf16_lo(cw.y)), o3 = fmaf(alpha, pv[3], bf16_hi(cw.y));
+        *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (col + e >= N) break;
+        if constexpr (std::is_same<TC, float>::value) {
+          p[e] = fmaf(alpha, pv[e], p[e]);
+        } else {
+          const float o = fmaf(alpha, pv[e], __builtin_bit_cast(float, (uint32_t)p[e] << 16));
+          p[e] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xFFFFu);
+        }
+      }
+    }
+  }
+}
+
 template <int R>
 static hipError_t lora_rank(const void* x, bool x_bf16, int64_t ldx, const void* a, const void* b, bool ab_bf16,
                             int64_t lda, int64_t ldb, float alpha, int64_t m, int64_t n, int64_t k, int64_t r,
@@ -168,19 +358,38 @@ static hipError_t lora_rank(const void* x, bool x_bf16, int64_t ldx, const void*
   hipLaunchKernelGGL((k_lora_down<TX, TA, R>), gd, bd, 0, stream, (const TX*)x, ldx, (const TA*)a, lda, (int)m,    \
                      (int)k, (int)r, t)
   if (x_bf16) {
-    if (ab_bf16) TP_DOWN(uint16_t, uint16_t); else TP_DOWN(uint16_t, float);
+    if (ab_bf16)
+      hipLaunchKernelGGL((k_lora_down_mfma<R>), dim3((unsigned)((m + 15) / 16)), dim3(512), 0, stream,
+                         (const uint16_t*)x, ldx, (const uint16_t*)a, lda, (int)m, (int)k, (int)r, t);
+    else
+      TP_DOWN(uint16_t, float);
   } else {
     if (ab_bf16) TP_DOWN(float, uint16_t); else TP_DOWN(float, float);
   }
 #undef TP_DOWN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 gu((unsigned)((n + LU_BN - 1) / LU_BN), (unsigned)((m + LU_BM - 1) / LU_BM)), bu(256);
+  // Up: one flattened grid of (row block, column block) pairs; both kernels'
+  // column blocks are 256 wide.
+  const int64_t nbn = (n + 255) / 256;
+  const int64_t rows_per = ab_bf16 ? 16 : LU_BM;
+  const int64_t blocks = (m + rows_per - 1) / rows_per * nbn;
+  if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
+  // C may be aligned to its element only; the vector accesses of the matrix
+  // unit path need 16 (fp32) or 8 (bf16) bytes for the base and the pitch.
+  const uintptr_t cva = c_bf16 ? 8 : 16;
+  const int cvec = ((uintptr_t)c % cva == 0) && ((uintptr_t)(ldc * (c_bf16 ? 2 : 4)) % cva == 0);
+  const dim3 gu((unsigned)blocks), bu(256);
 #define TP_UP(TB, TC)                                                                                           \
   hipLaunchKernelGGL((k_lora_up_add<TB, TC, R>), gu, bu, 0, stream, (const float*)t, (const TB*)b, ldb, alpha,      \
-                     (int)m, (int)n, (int)r, (TC*)c, ldc)
+                     (int)m, (int)n, (int)r, (TC*)c, ldc, (int)nbn)
   if (ab_bf16) {
-    if (c_bf16) TP_UP(uint16_t, uint16_t); else TP_UP(uint16_t, float);
+    if (c_bf16)
+      hipLaunchKernelGGL((k_lora_up_mfma<uint16_t, R>), gu, bu, 0, stream, (const float*)t, (const uint16_t*)b, ldb,
+                         alpha, (int)m, (int)n, (int)r, (uint16_t*)c, ldc, (int)nbn, cvec);
+    else
+      hipLaunchKernelGGL((k_lora_up_mfma<float, R>), gu, bu, 0, stream, (const float*)t, (const uint16_t*)b, ldb,
+                         alpha, (int)m, (int)n, (int)r, (float*)c, ldc, (int)nbn, cvec);
   } else {
     if (c_bf16) TP_UP(float, uint16_t); else TP_UP(float, float);
   }

@@ -99,3 +99,23 @@ def test_lora_rotated_domain_and_views():
     assert np.allclose(f64(view), ref, rtol=1e-4, atol=1e-5)
     assert torch.all(cbuf[0] == 4.0) and torch.all(cbuf[-1] == 4.0)
     assert torch.all(cbuf[:, :4] == 4.0) and torch.all(cbuf[:, 4 + n:] == 4.0)
+
+
+@pytest.mark.parametrize("cd,off,pad", [("f32", 1, 9), ("f32", 0, 11), ("bf16", 1, 9), ("bf16", 0, 11)])
+def test_lora_matrix_unit_views(cd, off, pad):
+    """bf16 operands (the matrix-unit kernels) into C views whose base and
+    pitch are aligned to the element only (off 1, pitch n + 9: element by
+    element) or to 16 bytes (off 0, pitch n + 11: vector accesses with a
+    ragged column tail); ragged m, n and r (partial lora_b vectors)."""
+    d = dev()
+    m, n, k, r = 37, 301, 512, 13
+    announce("tp_lora_add matrix-unit path, C view", cd, off, pad, m, n, k, r)
+    x, a, b, c = _lora_inputs(m, n, k, r, seed=50 + off + pad, xd="bf16", abd="bf16", cd=cd)
+    dt = torch.float32 if cd == "f32" else torch.bfloat16
+    cbuf = torch.full((m + 2, n + pad), 4.0, dtype=dt, device=d)
+    cbuf[1:1 + m, off:off + n] = c.to(d)
+    view = cbuf[1:1 + m, off:off + n]
+    tp.tp_lora_add(view, x.to(d), a.to(d), _padded_b(b, d), 0.6)
+    _check(view, c, x, a, b, 0.6, bf16_out=cd == "bf16")
+    assert torch.all(cbuf[0] == 4.0) and torch.all(cbuf[-1] == 4.0)
+    assert torch.all(cbuf[:, :off] == 4.0) and torch.all(cbuf[:, off + n:] == 4.0)
