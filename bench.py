@@ -371,13 +371,19 @@ def next_rows(args, cpu):
     del q8, s8, wh, q4, s4
 
     # NEXT-4: a LoRA side path (rank 32 and 64) added into the W8A8 qkv
-    # projection's fp32 output, against the product's own time.
+    # projection's fp32 output, against the product's own time: as a second
+    # pass over C (tp_lora_add), and in the product's store (tp_lora_down, then
+    # tp_qgemm_w8a8_prequantized_lora against tp_qgemm_w8a8_prequantized).
     wl = W.DIT_QKV
     x, w = W.generate(wl)
     xd = x.to(d)
     q8, s8 = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
     y = tp.tp_qgemm_w8a8(xd, q8, s8)
     prod_us = _time_us(torch, lambda: tp.tp_qgemm_w8a8(xd, q8, s8, out=y))
+    qa, sa = tp.tp_quantize_rows_int8(xd)
+    y2 = torch.empty_like(y)
+    pre_us = _time_us(torch, lambda: tp.tp_qgemm_w8a8_prequantized(qa, sa, q8, s8, out=y2))
+    tbuf = torch.empty((wl.m, 64), dtype=torch.float32, device=d)
     for r in (32, 64):
         a = (torch.randn((r, wl.k), device=d) * 0.02).to(torch.bfloat16)
         b = (torch.randn((wl.n, r), device=d) * 0.02).to(torch.bfloat16)
@@ -391,6 +397,12 @@ def next_rows(args, cpu):
                                                 "algorithmic_bytes": int(alg)},
                "vs_product": f"{us / prod_us * 100:.1f}% of the W8A8 qkv product ({prod_us:.1f} us incl. its "
                              f"activation quantization)"}
+        fus_us = _time_us(torch, lambda: (tp.tp_lora_down(xd, a, t=tbuf),
+                                          tp.tp_qgemm_w8a8_prequantized_lora(qa, sa, q8, s8, tbuf, b, 0.8, out=y2)))
+        row["in_store"] = {"us": round(fus_us, 2), "product_alone_us": round(pre_us, 2),
+                           "extra_us": round(fus_us - pre_us, 2),
+                           "note": f"tp_lora_down + tp_qgemm_w8a8_prequantized_lora: the side path costs "
+                                   f"{(fus_us - pre_us) / pre_us * 100:.1f}% of the prequantized product"}
         if cpu:
             import oracle
             rows = 64

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 6
+#define TP_ABI_VERSION 7
 
 typedef enum tp_status {
   TP_OK = 0,
@@ -208,6 +208,23 @@ tp_status tp_lora_add(const void* x, tp_dtype x_dtype, int64_t ldx, const void* 
                       int64_t m, int64_t n, int64_t k, int64_t r, void* c, tp_dtype c_dtype,
                       int64_t ldc, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * tp_lora_down -- the first half of the LoRA side path on its own (same
+ * section), for tp_qgemm_w8a8_prequantized_lora:
+ *
+ *   T[i, t] = sum_q X[i, q] * lora_a[t, q]   (fp32, summed in a fixed order)
+ *
+ *   x        [m, k] (TP_F32 or TP_BF16), row pitch ldx; lora_a [r, k]
+ *            (a_dtype), row pitch lda; 16-byte aligned rows; 1 <= r <= 64;
+ *            k a multiple of 256.
+ *   t        fp32 [m, 64], rows of 64 floats (zeros past r), 16-byte aligned,
+ *            t_bytes >= m * 256; must not overlap x or lora_a.
+ * The same T as tp_lora_add computes internally (bit for bit).
+ */
+tp_status tp_lora_down(const void* x, tp_dtype x_dtype, int64_t ldx, const void* lora_a,
+                       tp_dtype a_dtype, int64_t lda, int64_t m, int64_t k, int64_t r, float* t,
+                       size_t t_bytes, hipStream_t stream);
+
 /* out_kind of tp_swiglu_rotate. */
 #define TP_FFN_OUT_I8 0   /* int8 codes [m, k] and fp32 scales [m] */
 #define TP_FFN_OUT_BF16 1 /* rotated bf16 rows [m, k]              */
@@ -340,6 +357,32 @@ tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float
                                      void* c, tp_dtype c_dtype, int64_t ldc, int32_t* acc_out,
                                      int64_t ld_acc, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
+
+/*
+ * tp_qgemm_w8a8_prequantized_lora -- tp_qgemm_w8a8_prequantized with a LoRA
+ * side path added in the product's store (kvad-gpu internals, section
+ * "Pictures, which are not tokens": the side path is added into the layer's
+ * output, here by the kernel that writes it):
+ *
+ *   C[i, c] = fl(fl((float(acc[i, c]) * sa[i]) * w_scales[c]) + alpha * L[i, c])
+ *   L[i, c] = sum_t T[i, t] * lora_b[c, t]   (fp32)
+ *
+ *   qa, sa, q, w_scales, m, n, k, workspace: as tp_qgemm_w8a8_prequantized.
+ *   c        fp32 [m, n], row pitch ldc (fp32 only).
+ *   t        fp32 [m, 64] from tp_lora_down (rows of 64 floats, zeros past r).
+ *   lora_b   bf16 [n, r], row pitch ldb elements (16-byte aligned rows);
+ *            1 <= r <= 64.
+ * Large outputs run it in the product kernel's store; the others (few rows,
+ * split K) store the product and then add the side path with the up half of
+ * tp_lora_add. Both give the bits of tp_qgemm_w8a8_prequantized followed by
+ * tp_lora_add with bf16 x, lora_a and lora_b.
+ */
+tp_status tp_qgemm_w8a8_prequantized_lora(const int8_t* qa, int64_t ldqa, const float* sa,
+                                          const int8_t* q, int64_t ldq, const float* w_scales,
+                                          int64_t m, int64_t n, int64_t k, float* c, int64_t ldc,
+                                          const float* t, const void* lora_b, int64_t ldb, int64_t r,
+                                          float alpha, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
 
 /*
  * tp_qgemm_w4a8 -- the int4 weights of tp_qgemm_w4 (one fp32 scale per row

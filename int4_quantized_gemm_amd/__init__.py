@@ -227,6 +227,33 @@ def tp_qgemm_w8a8_prequantized(qa, sa, q, scales, out_dtype=torch.float32, out=N
     return out
 
 
+def tp_qgemm_w8a8_prequantized_lora(qa, sa, q, scales, t, lora_b, alpha, out=None, workspace=None, stream=None):
+    """C = (float(qa . q^T) * sa[m]) * s[n] + alpha * T . lora_b^T in fp32, the
+    side path added in the product's store; T from tp_lora_down, lora_b bf16
+    [n, r]."""
+    ldqa = _mat(qa, "qa")
+    m, k = qa.shape
+    n = q.shape[0]
+    r = lora_b.shape[1]
+    ldq = _mat(q, "q")
+    _vec(sa, "sa", m)
+    _vec(scales, "w_scales", n)
+    if t.dtype != torch.float32 or t.shape != (m, 64) or not t.is_contiguous():
+        raise ValueError("t must be contiguous fp32 [m, 64] (from tp_lora_down)")
+    if lora_b.dtype != torch.bfloat16 or lora_b.shape[0] != n:
+        raise ValueError("lora_b must be bf16 [n, r]")
+    ldb = _mat(lora_b, "lora_b")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=qa.device)
+    ldc = _mat(out, "out")
+    ws, ws_bytes = _workspace(_lib.TP_OP_QGEMM_W8A8_PREQUANTIZED, m, n, k, TP_A_PREROTATED, qa.device, workspace)
+    _lib.check(_lib.load().tp_qgemm_w8a8_prequantized_lora(qa.data_ptr(), ldqa, sa.data_ptr(), q.data_ptr(), ldq,
+                                                           scales.data_ptr(), m, n, k, out.data_ptr(), ldc,
+                                                           t.data_ptr(), lora_b.data_ptr(), ldb, r, float(alpha),
+                                                           _ptr(ws), ws_bytes, _stream(stream)))
+    return out
+
+
 def tp_qgemm_w4a8(a, q4, scales, rotate=True, out_dtype=torch.float32, out=None, want_codes=False, workspace=None,
                   stream=None):
     """Per-token int8 activations x int4 weights with one scale per (row,
@@ -311,6 +338,22 @@ def tp_requantize_weights(q, scales, bits_in, bits_out, q_out=None, scales_out=N
 def tp_lora_workspace_size(m, r):
     """Bytes of workspace tp_lora_add needs for m rows at rank r."""
     return int(_lib.load().tp_lora_workspace_size(m, r))
+
+
+def tp_lora_down(x, lora_a, t=None, stream=None):
+    """T = x . lora_a^T in fp32 rows of 64 (zeros past r): the first half of
+    the side path, for tp_qgemm_w8a8_prequantized_lora. Returns T [m, 64]."""
+    ldx = _mat(x, "x")
+    m, k = x.shape
+    r = lora_a.shape[0]
+    if lora_a.shape[1] != k:
+        raise ValueError("lora_a must be [r, k]")
+    lda = _mat(lora_a, "lora_a")
+    if t is None:
+        t = torch.empty((m, 64), dtype=torch.float32, device=x.device)
+    _lib.check(_lib.load().tp_lora_down(x.data_ptr(), _dt(x), ldx, lora_a.data_ptr(), _dt(lora_a), lda, m, k, r,
+                                        t.data_ptr(), t.numel() * t.element_size(), _stream(stream)))
+    return t
 
 
 def tp_lora_add(c, x, lora_a, lora_b, alpha, workspace=None, stream=None):

@@ -45,6 +45,9 @@ SIGNATURES = {
     "tp_lora_workspace_size": (_sz, [_i64, _i64]),
     "tp_lora_add": (_int, [_p, _int, _i64, _p, _p, _int, _i64, _i64, ctypes.c_float, _i64, _i64, _i64, _i64, _p, _int,
                            _i64, _p, _sz, _p]),
+    "tp_lora_down": (_int, [_p, _int, _i64, _p, _int, _i64, _i64, _i64, _i64, _p, _sz, _p]),
+    "tp_qgemm_w8a8_prequantized_lora": (_int, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64,
+                                               _i64, ctypes.c_float, _p, _sz, _p]),
     "tp_dequantize_unrotate": (_int, [_p, _int, _i64, _p, _i64, _i64, _p, _int, _i64, _p]),
     "tp_requantize_weights": (_int, [_p, _int, _i64, _p, _i64, _i64, _int, _p, _i64, _p, _p]),
     "tp_swiglu_rotate": (_int, [_p, _i64, _p, _i64, _int, _i64, _i64, _int, _p, _i64, _p, _p]),

@@ -316,6 +316,27 @@ tp_status tp_lora_add(const void* x, tp_dtype x_dtype, int64_t ldx, const void* 
                     "lora launch");
 }
 
+tp_status tp_lora_down(const void* x, tp_dtype x_dtype, int64_t ldx, const void* lora_a, tp_dtype a_dtype,
+                       int64_t lda, int64_t m, int64_t k, int64_t r, float* t, size_t t_bytes, hipStream_t stream) {
+  if (!dtype_ok(x_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "x_dtype %d is not TP_F32 or TP_BF16", (int)x_dtype);
+  if (!dtype_ok(a_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "a_dtype %d is not TP_F32 or TP_BF16", (int)a_dtype);
+  TP_TRY(check_sizes(m, 0, k));
+  if (r < 1 || r > 64) return fail(TP_ERR_BAD_SHAPE, "rank r=%lld outside [1, 64]", (long long)r);
+  const int64_t ex = dtype_size(x_dtype), ea = dtype_size(a_dtype);
+  Extent e_x, e_a, e_t;
+  TP_TRY(check_matrix("x", x, m, k * ex, ldx, ex, &e_x));
+  TP_TRY(check_matrix("lora_a", lora_a, r, k * ea, lda, ea, &e_a));
+  if (m > 0 && (int64_t)t_bytes < m * 64 * 4)
+    return fail(TP_ERR_WORKSPACE_TOO_SMALL, "t of %zu bytes, %lld needed (m rows of 64 floats)", t_bytes,
+                (long long)(m * 64 * 4));
+  TP_TRY(check_matrix("t", t, m, 64 * 4, 64, 4, &e_t));
+  if (overlaps(e_t, e_x) || overlaps(e_t, e_a)) return fail(TP_ERR_BAD_ALIASING, "t overlaps an input");
+  if (m == 0) return ok();
+  return hip_status(tp::launch_lora_down(x, x_dtype == TP_BF16, ldx, lora_a, a_dtype == TP_BF16, lda, m, k, r, t,
+                                         stream),
+                    "lora down launch");
+}
+
 tp_status tp_dequantize_unrotate(const void* q, int bits, int64_t ldq_bytes, const float* scales, int64_t n,
                                  int64_t k, void* w, tp_dtype w_dtype, int64_t ldw, hipStream_t stream) {
   if (!dtype_ok(w_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "w_dtype %d is not TP_F32 or TP_BF16", (int)w_dtype);
@@ -505,10 +526,20 @@ tp_status act8_product(int kind, const void* a, tp_dtype a_dtype, int64_t lda, i
   return hip_status(tp::launch_qgemm(g, stream), "product launch");
 }
 
+// The side path of tp_qgemm_w8a8_prequantized_lora: T fp32 [m, 64] (rows of
+// 64 floats, zeros past r) and lora_b bf16 [n, r]; fp32 C only.
+struct LoraIn {
+  const float* t;
+  const void* b;
+  int64_t ldb;
+  int64_t r;
+  float alpha;
+};
+
 tp_status prequantized_product(int kind, const int8_t* qa, int64_t ldqa, const float* sa, const void* q, int64_t ldq,
                                const float* w_scales, int64_t m, int64_t n, int64_t k, void* c, tp_dtype c_dtype,
                                int64_t ldc, int32_t* acc_out, int64_t ld_acc, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+                               size_t workspace_bytes, hipStream_t stream, const LoraIn* lora = nullptr) {
   const bool w4 = kind == tp::GEMM_W4A8;
   const tp_op op = w4 ? TP_OP_QGEMM_W4A8_PREQUANTIZED : TP_OP_QGEMM_W8A8_PREQUANTIZED;
   if (!dtype_ok(c_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "c_dtype %d is not TP_F32 or TP_BF16", (int)c_dtype);
@@ -525,12 +556,19 @@ tp_status prequantized_product(int kind, const int8_t* qa, int64_t ldqa, const f
   TP_TRY(check_vector("w_scales", w_scales, ns, &es));
   TP_TRY(check_matrix("c", c, m, n * dtype_size(c_dtype), ldc, dtype_size(c_dtype), &ec, dtype_size(c_dtype)));
   if (acc_out) TP_TRY(check_matrix("acc_out", acc_out, m, n * 4, ld_acc, 4, &eacc, 4));
+  Extent et, eb;
+  if (lora) {
+    if (c_dtype != TP_F32) return fail(TP_ERR_UNSUPPORTED_DTYPE, "the side path adds into fp32 C only");
+    if (lora->r < 1 || lora->r > 64) return fail(TP_ERR_BAD_SHAPE, "rank r=%lld outside [1, 64]", (long long)lora->r);
+    TP_TRY(check_matrix("t", lora->t, m, 64 * 4, 64, 4, &et));
+    TP_TRY(check_matrix("lora_b", lora->b, n, lora->r * 2, lora->ldb, 2, &eb));
+  }
   WsLayout wl;
   Extent ew;
   if (!workspace_layout(op, m, n, k, TP_A_PREROTATED, true, &wl))
     return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
   TP_TRY(check_workspace(wl, workspace, workspace_bytes, &ew));
-  const Extent* ins[] = {&eqa, &esa, &eq, &es};
+  const Extent* ins[] = {&eqa, &esa, &eq, &es, &et, &eb};
   for (const Extent* i : ins)
     if (overlaps(ec, *i) || overlaps(eacc, *i) || overlaps(ew, *i))
       return fail(TP_ERR_BAD_ALIASING, "an output or the workspace overlaps an input");
@@ -554,6 +592,13 @@ tp_status prequantized_product(int kind, const int8_t* qa, int64_t ldqa, const f
   g.acc_out = acc_out;
   g.ld_acc = ld_acc;
   g.part = wl.total > 0 ? workspace : nullptr;
+  if (lora) {
+    g.lora.t = lora->t;
+    g.lora.b = (const uint16_t*)lora->b;
+    g.lora.ldb = lora->ldb;
+    g.lora.r = (int)lora->r;
+    g.lora.alpha = lora->alpha;
+  }
   return hip_status(tp::launch_qgemm(g, stream), "product launch");
 }
 
@@ -573,6 +618,16 @@ tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float
                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return prequantized_product(tp::GEMM_W8A8, qa, ldqa, sa, q, ldq, w_scales, m, n, k, c, c_dtype, ldc, acc_out,
                               ld_acc, workspace, workspace_bytes, stream);
+}
+
+tp_status tp_qgemm_w8a8_prequantized_lora(const int8_t* qa, int64_t ldqa, const float* sa, const int8_t* q,
+                                          int64_t ldq, const float* w_scales, int64_t m, int64_t n, int64_t k,
+                                          float* c, int64_t ldc, const float* t, const void* lora_b, int64_t ldb,
+                                          int64_t r, float alpha, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  const LoraIn lora{t, lora_b, ldb, r, alpha};
+  return prequantized_product(tp::GEMM_W8A8, qa, ldqa, sa, q, ldq, w_scales, m, n, k, c, TP_F32, ldc, nullptr, 0,
+                              workspace, workspace_bytes, stream, &lora);
 }
 
 tp_status tp_qgemm_w4a8(const void* a, tp_dtype a_dtype, int64_t lda, int a_flags, const uint8_t* q4,

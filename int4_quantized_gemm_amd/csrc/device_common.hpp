@@ -46,6 +46,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// fp32 v = hi + mid + lo exactly, each part bf16 (round to nearest even at
+// each step; each residual is exact in fp32 and the last one fits in 8 bits).
+__device__ __forceinline__ void split3_bf16(const float (&v)[8], bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
+  u32x4_t h, m, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a0 = v[2 * e], a1 = v[2 * e + 1];
+    const uint32_t hw = pack_bf16x2(a0, a1);
+    const float r0 = a0 - bf16_lo(hw), r1 = a1 - bf16_hi(hw);
+    const uint32_t mw = pack_bf16x2(r0, r1);
+    const uint32_t lw = pack_bf16x2(r0 - bf16_lo(mw), r1 - bf16_hi(mw));
+    h[e] = hw;
+    m[e] = mw;
+    l[e] = lw;
+  }
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  mid = __builtin_bit_cast(bf16x8_t, m);
+  lo = __builtin_bit_cast(bf16x8_t, l);
+}
+
 // Exchange with the lane whose index differs in bit log2(MASK), inside each
 // 32-lane half of the wave (ds_swizzle bit-mask mode: and 0x1f, xor MASK).
 template <int MASK>

@@ -131,6 +131,22 @@ int64_t qgemm_partial_bytes(int kind, int64_t m, int64_t n, int64_t k) {
 template <int KIND>
 static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
   SkPlan sp;
+  if (g.lora.t) {
+    // The side path rides in the store of the single-pass W8A8 kernel; other
+    // plans (few rows, split K) store the product and then add the side path
+    // with the standalone up-projection, whose arithmetic is the same (fp32 C:
+    // the same two roundings, the same MFMA sequence).
+    const bool fused = KIND == GEMM_W8A8 && !g.c_bf16 && !g.acc_out && !skinny_plan(KIND, g.m, g.n, g.k, &sp) &&
+                       pick_plan(KIND, g.m, g.n, g.k).splits == 1;
+    if (!fused) {
+      GemmArgs g2 = g;
+      g2.lora.t = nullptr;
+      const hipError_t e = launch_kind<KIND>(g2, stream);
+      if (e != hipSuccess) return e;
+      return launch_lora_up(g.lora.t, g.lora.b, true, g.lora.ldb, g.lora.alpha, g.m, g.n, g.lora.r, g.c, g.c_bf16,
+                            g.ldc, stream);
+    }
+  }
   if (skinny_plan(KIND, g.m, g.n, g.k, &sp)) {
     if (sp.splits > 1 && !g.part) return hipErrorInvalidValue;
     return launch_skinny<KIND>(g, sp, stream);

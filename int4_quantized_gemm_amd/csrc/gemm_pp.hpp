@@ -173,12 +173,12 @@ struct PPCfg {
 // splits in order and applies the epilogue. sps is a multiple of 4 (whole
 // 256-groups).
 template <int KIND, int BM, int BN, int WM, int WN, int NSTAGE, bool OUT_BF16, bool ACC_OUT, bool PARTIAL,
-          int EWN = 0>
+          int EWN = 0, bool LORA = false>
 __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
     const uint8_t* __restrict__ A, int64_t lda_bytes, const uint8_t* __restrict__ B, int64_t ldb_bytes,
     const float* __restrict__ sw, const float* __restrict__ sa, int M, int N, int K, void* __restrict__ Cv,
     int64_t ldc, int32_t* __restrict__ acc_out, int64_t ld_acc, int tiles_m, int tiles_n, int gm, int sps,
-    void* __restrict__ part) {
+    void* __restrict__ part, LoraEpi lora) {
   using Cfg = PPCfg<KIND, BM, BN, WM, WN, NSTAGE>;
   constexpr bool I8 = Cfg::I8;
   constexpr int FM = Cfg::FM, FN = Cfg::FN, NWN = Cfg::NWN;
@@ -614,6 +614,88 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
     }
   };
   typedef typename std::conditional<OUT_BF16, __bf16, float>::type out_t;
+  if constexpr (LORA) {
+    // LoRA side path in the store (fp32 C): out = fma(alpha, L, value) with
+    // L = T . lora_b^T for this fragment, on the same MFMA sequence as the
+    // standalone up-projection (T split exactly into three bf16 parts; the
+    // two small parts first), so both paths give the same bits. The wave's
+    // lora_b fragments are loaded once; T rows are fetched one fragment row
+    // ahead so that no load latency sits between two fragments.
+    static_assert(KIND == GEMM_W8A8, "the side path rides in the W8A8 store only");
+    const bool two = lora.r > 32;  // 32-deep steps over the rank: 1 or 2
+    // The product's values first, into the accumulators' registers (the
+    // epilogue scales are then dead, which makes room for the side path).
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_bit_cast(acc_t, f32x4_t{value(i, j, 0), value(i, j, 1), value(i, j, 2), value(i, j, 3)});
+    bf16x8_t lb[FN][2];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn0 + j * 16 + r16;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int j0 = 32 * s + 8 * g4;
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (col < N && j0 < lora.r) {
+          const uint16_t* brow = lora.b + (int64_t)col * lora.ldb + j0;
+          if (j0 + 8 <= lora.r) {
+            w = *reinterpret_cast<const u32x4_t*>(brow);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const uint32_t lo = j0 + e < lora.r ? brow[e] : 0u, hi = j0 + e + 1 < lora.r ? brow[e + 1] : 0u;
+              w[e >> 1] = lo | (hi << 16);
+            }
+          }
+        }
+        lb[j][s] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    }
+    auto fetch_t = [&](int i, float (&v)[2][8]) {
+      const int trow = m0 + wm0 + i * 16 + r16;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (trow < M && (s == 0 || two)) {
+          load8(lora.t + (int64_t)trow * 64 + 32 * s + 8 * g4, v[s]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[s][e] = 0.f;
+        }
+      }
+    };
+    float tv[2][8];
+    fetch_t(0, tv);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      bf16x8_t th[2], tm[2], tl[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) split3_bf16(tv[s], th[s], tm[s], tl[s]);
+      if (i + 1 < FM) fetch_t(i + 1, tv);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn0 + j * 16 + r16;
+        f32x4_t L = {0.f, 0.f, 0.f, 0.f};
+        L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl[0], lb[j][0], L, 0, 0, 0);
+        L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tm[0], lb[j][0], L, 0, 0, 0);
+        if (two) {
+          L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl[1], lb[j][1], L, 0, 0, 0);
+          L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tm[1], lb[j][1], L, 0, 0, 0);
+        }
+        L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th[0], lb[j][0], L, 0, 0, 0);
+        if (two) L = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th[1], lb[j][1], L, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm0 + i * 16 + g4 * 4 + r;
+          if (row < M && col < N)
+            reinterpret_cast<float*>(Cv)[(int64_t)row * ldc + col] =
+                fmaf(lora.alpha, L[r], __builtin_bit_cast(f32x4_t, acc[i][j])[r]);
+        }
+      }
+    }
+    return;
+  }
   const int row0 = m0 + wm0 + g4 * 4, col0 = n0 + wn0 + r16;
   out_t* cbase = reinterpret_cast<out_t*>(Cv) + (int64_t)row0 * ldc + col0;
   int32_t* abase = ACC_OUT ? acc_out + (int64_t)row0 * ld_acc + col0 : nullptr;
@@ -658,12 +740,20 @@ static hipError_t launch_pp(const GemmArgs& g, hipStream_t stream, int gm = 8, i
 #define TP_LAUNCH_PP(OB, AO, PA)                                                                                  \
   hipLaunchKernelGGL((k_qgemm_pp<KIND, BM, BN, WM, WN, NSTAGE, OB, AO, PA, EWN>), grid, block, 0, stream, a, lda_bytes, b, \
                      g.ldb, g.w_scales, g.a_scales, (int)g.m, (int)g.n, (int)g.k, g.c, g.ldc, g.acc_out, g.ld_acc,    \
-                     tiles_m, tiles_n, gm, sps, g.part)
+                     tiles_m, tiles_n, gm, sps, g.part, g.lora)
   if (splits > 1) {
     TP_LAUNCH_PP(false, false, true);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_reduce<KIND>(g, splits, stream);
+  }
+  if constexpr (KIND == GEMM_W8A8) {
+    if (g.lora.t) {  // fp32 C, no int32 output (checked by the caller)
+      hipLaunchKernelGGL((k_qgemm_pp<KIND, BM, BN, WM, WN, NSTAGE, false, false, false, EWN, true>), grid, block, 0,
+                         stream, a, lda_bytes, b, g.ldb, g.w_scales, g.a_scales, (int)g.m, (int)g.n, (int)g.k, g.c,
+                         g.ldc, g.acc_out, g.ld_acc, tiles_m, tiles_n, gm, sps, g.part, g.lora);
+      return hipGetLastError();
+    }
   }
   if (KIND == GEMM_W8A8 && g.acc_out) {
     if (g.c_bf16) TP_LAUNCH_PP(true, true, false); else TP_LAUNCH_PP(false, true, false);

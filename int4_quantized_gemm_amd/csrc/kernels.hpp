@@ -25,10 +25,15 @@ hipError_t launch_requantize(const void* q_in, int bits_in, int64_t ldq_in, cons
                              int bits_out, void* q_out, int64_t ldq_out, float* s_out, hipStream_t stream);
 
 // LoRA side path: c += alpha * (x . a^T) . b^T with a [r, k], b [n, r]
-// (r <= 64); t is fp32 [m, r] scratch.
+// (r <= 64); t is fp32 [m, 64] (rows of 64, zeros past r): the down half
+// writes it, the up half reads it.
 hipError_t launch_lora_add(const void* x, bool x_bf16, int64_t ldx, const void* a, const void* b, bool ab_bf16,
                            int64_t lda, int64_t ldb, float alpha, int64_t m, int64_t n, int64_t k, int64_t r, void* c,
                            bool c_bf16, int64_t ldc, float* t, hipStream_t stream);
+hipError_t launch_lora_down(const void* x, bool x_bf16, int64_t ldx, const void* a, bool a_bf16, int64_t lda,
+                            int64_t m, int64_t k, int64_t r, float* t, hipStream_t stream);
+hipError_t launch_lora_up(const float* t, const void* b, bool b_bf16, int64_t ldb, float alpha, int64_t m, int64_t n,
+                          int64_t r, void* c, bool c_bf16, int64_t ldc, hipStream_t stream);
 
 // FFN middle: h = bf16(silu(g) * u), rotated per 256-group, then int8 codes
 // with one scale per row (out_i8) or bf16 rows (scales unused).
@@ -36,6 +41,16 @@ hipError_t launch_swiglu_rotate(const void* g, int64_t ldg, const void* u, int64
                                 int64_t k, bool out_i8, void* y, int64_t ldy, float* scales, hipStream_t stream);
 
 enum GemmKind { GEMM_W8 = 0, GEMM_W4 = 1, GEMM_W8A8 = 2, GEMM_W4A8 = 3 };
+
+// A LoRA side path added in a product's store (t == nullptr: none):
+// C = product + alpha * T . b^T, T fp32 [m, 64] (zeros past r), b bf16 [n, r].
+struct LoraEpi {
+  const float* t;
+  const uint16_t* b;
+  int64_t ldb;  // elements
+  int r;        // 1 .. 64
+  float alpha;
+};
 
 struct GemmArgs {
   int kind;                 // GemmKind
@@ -52,6 +67,7 @@ struct GemmArgs {
   int32_t* acc_out;         // optional int32 [m, n] (W8A8 only)
   int64_t ld_acc;
   void* part;               // split-K partial sums, qgemm_partial_bytes() bytes (may be null when that is 0)
+  LoraEpi lora;             // fp32 C only
 };
 
 hipError_t launch_qgemm(const GemmArgs& args, hipStream_t stream);

@@ -224,26 +224,6 @@ __global__ __launch_bounds__(512) void k_lora_down_mfma(const uint16_t* __restri
   }
 }
 
-// fp32 v = hi + mid + lo exactly, each part bf16 (round to nearest even at
-// each step; each residual is exact in fp32 and the last one fits in 8 bits).
-__device__ __forceinline__ void split3_bf16(const float (&v)[8], bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
-  u32x4_t h, m, l;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float a0 = v[2 * e], a1 = v[2 * e + 1];
-    const uint32_t hw = pack_bf16x2(a0, a1);
-    const float r0 = a0 - bf16_lo(hw), r1 = a1 - bf16_hi(hw);
-    const uint32_t mw = pack_bf16x2(r0, r1);
-    const uint32_t lw = pack_bf16x2(r0 - bf16_lo(mw), r1 - bf16_hi(mw));
-    h[e] = hw;
-    m[e] = mw;
-    l[e] = lw;
-  }
-  hi = __builtin_bit_cast(bf16x8_t, h);
-  mid = __builtin_bit_cast(bf16x8_t, m);
-  lo = __builtin_bit_cast(bf16x8_t, l);
-}
-
 // Up, bf16 lora_B: a block owns 16 rows x 256 columns of C, a wave 64 of the
 // columns. T (fp32) is split exactly into three bf16 parts; the two small
 // parts are summed first and the large part last, so the result carries
@@ -350,29 +330,32 @@ __global__ __launch_bounds__(256) void k_lora_up_mfma(const float* __restrict__ 
 }
 
 template <int R>
-static hipError_t lora_rank(const void* x, bool x_bf16, int64_t ldx, const void* a, const void* b, bool ab_bf16,
-                            int64_t lda, int64_t ldb, float alpha, int64_t m, int64_t n, int64_t k, int64_t r,
-                            void* c, bool c_bf16, int64_t ldc, float* t, hipStream_t stream) {
+static hipError_t lora_down_r(const void* x, bool x_bf16, int64_t ldx, const void* a, bool a_bf16, int64_t lda,
+                              int64_t m, int64_t k, int64_t r, float* t, hipStream_t stream) {
   const dim3 gd((unsigned)((m + LD_BM - 1) / LD_BM)), bd(256);
 #define TP_DOWN(TX, TA)                                                                                         \
   hipLaunchKernelGGL((k_lora_down<TX, TA, R>), gd, bd, 0, stream, (const TX*)x, ldx, (const TA*)a, lda, (int)m,    \
                      (int)k, (int)r, t)
   if (x_bf16) {
-    if (ab_bf16)
+    if (a_bf16)
       hipLaunchKernelGGL((k_lora_down_mfma<R>), dim3((unsigned)((m + 15) / 16)), dim3(512), 0, stream,
                          (const uint16_t*)x, ldx, (const uint16_t*)a, lda, (int)m, (int)k, (int)r, t);
     else
       TP_DOWN(uint16_t, float);
   } else {
-    if (ab_bf16) TP_DOWN(float, uint16_t); else TP_DOWN(float, float);
+    if (a_bf16) TP_DOWN(float, uint16_t); else TP_DOWN(float, float);
   }
 #undef TP_DOWN
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // Up: one flattened grid of (row block, column block) pairs; both kernels'
+  return hipGetLastError();
+}
+
+template <int R>
+static hipError_t lora_up_r(const float* t, const void* b, bool b_bf16, int64_t ldb, float alpha, int64_t m,
+                            int64_t n, int64_t r, void* c, bool c_bf16, int64_t ldc, hipStream_t stream) {
+  // One flattened grid of (row block, column block) pairs; both kernels'
   // column blocks are 256 wide.
   const int64_t nbn = (n + 255) / 256;
-  const int64_t rows_per = ab_bf16 ? 16 : LU_BM;
+  const int64_t rows_per = b_bf16 ? 16 : LU_BM;
   const int64_t blocks = (m + rows_per - 1) / rows_per * nbn;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
   // C may be aligned to its element only; the vector accesses of the matrix
@@ -381,15 +364,15 @@ static hipError_t lora_rank(const void* x, bool x_bf16, int64_t ldx, const void*
   const int cvec = ((uintptr_t)c % cva == 0) && ((uintptr_t)(ldc * (c_bf16 ? 2 : 4)) % cva == 0);
   const dim3 gu((unsigned)blocks), bu(256);
 #define TP_UP(TB, TC)                                                                                           \
-  hipLaunchKernelGGL((k_lora_up_add<TB, TC, R>), gu, bu, 0, stream, (const float*)t, (const TB*)b, ldb, alpha,      \
-                     (int)m, (int)n, (int)r, (TC*)c, ldc, (int)nbn)
-  if (ab_bf16) {
+  hipLaunchKernelGGL((k_lora_up_add<TB, TC, R>), gu, bu, 0, stream, t, (const TB*)b, ldb, alpha, (int)m, (int)n,   \
+                     (int)r, (TC*)c, ldc, (int)nbn)
+  if (b_bf16) {
     if (c_bf16)
-      hipLaunchKernelGGL((k_lora_up_mfma<uint16_t, R>), gu, bu, 0, stream, (const float*)t, (const uint16_t*)b, ldb,
-                         alpha, (int)m, (int)n, (int)r, (uint16_t*)c, ldc, (int)nbn, cvec);
+      hipLaunchKernelGGL((k_lora_up_mfma<uint16_t, R>), gu, bu, 0, stream, t, (const uint16_t*)b, ldb, alpha, (int)m,
+                         (int)n, (int)r, (uint16_t*)c, ldc, (int)nbn, cvec);
     else
-      hipLaunchKernelGGL((k_lora_up_mfma<float, R>), gu, bu, 0, stream, (const float*)t, (const uint16_t*)b, ldb,
-                         alpha, (int)m, (int)n, (int)r, (float*)c, ldc, (int)nbn, cvec);
+      hipLaunchKernelGGL((k_lora_up_mfma<float, R>), gu, bu, 0, stream, t, (const uint16_t*)b, ldb, alpha, (int)m,
+                         (int)n, (int)r, (float*)c, ldc, (int)nbn, cvec);
   } else {
     if (c_bf16) TP_UP(float, uint16_t); else TP_UP(float, float);
   }
@@ -397,12 +380,26 @@ static hipError_t lora_rank(const void* x, bool x_bf16, int64_t ldx, const void*
   return hipGetLastError();
 }
 
+hipError_t launch_lora_down(const void* x, bool x_bf16, int64_t ldx, const void* a, bool a_bf16, int64_t lda,
+                            int64_t m, int64_t k, int64_t r, float* t, hipStream_t stream) {
+  if (r <= 16) return lora_down_r<16>(x, x_bf16, ldx, a, a_bf16, lda, m, k, r, t, stream);
+  if (r <= 32) return lora_down_r<32>(x, x_bf16, ldx, a, a_bf16, lda, m, k, r, t, stream);
+  return lora_down_r<64>(x, x_bf16, ldx, a, a_bf16, lda, m, k, r, t, stream);
+}
+
+hipError_t launch_lora_up(const float* t, const void* b, bool b_bf16, int64_t ldb, float alpha, int64_t m, int64_t n,
+                          int64_t r, void* c, bool c_bf16, int64_t ldc, hipStream_t stream) {
+  if (r <= 16) return lora_up_r<16>(t, b, b_bf16, ldb, alpha, m, n, r, c, c_bf16, ldc, stream);
+  if (r <= 32) return lora_up_r<32>(t, b, b_bf16, ldb, alpha, m, n, r, c, c_bf16, ldc, stream);
+  return lora_up_r<64>(t, b, b_bf16, ldb, alpha, m, n, r, c, c_bf16, ldc, stream);
+}
+
 hipError_t launch_lora_add(const void* x, bool x_bf16, int64_t ldx, const void* a, const void* b, bool ab_bf16,
                            int64_t lda, int64_t ldb, float alpha, int64_t m, int64_t n, int64_t k, int64_t r, void* c,
                            bool c_bf16, int64_t ldc, float* t, hipStream_t stream) {
-  if (r <= 16) return lora_rank<16>(x, x_bf16, ldx, a, b, ab_bf16, lda, ldb, alpha, m, n, k, r, c, c_bf16, ldc, t, stream);
-  if (r <= 32) return lora_rank<32>(x, x_bf16, ldx, a, b, ab_bf16, lda, ldb, alpha, m, n, k, r, c, c_bf16, ldc, t, stream);
-  return lora_rank<64>(x, x_bf16, ldx, a, b, ab_bf16, lda, ldb, alpha, m, n, k, r, c, c_bf16, ldc, t, stream);
+  const hipError_t e = launch_lora_down(x, x_bf16, ldx, a, ab_bf16, lda, m, k, r, t, stream);
+  if (e != hipSuccess) return e;
+  return launch_lora_up(t, b, ab_bf16, ldb, alpha, m, n, r, c, c_bf16, ldc, stream);
 }
 
 }  // namespace tp

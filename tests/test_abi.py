@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.tp_abi_version() == 6
+    assert lib.tp_abi_version() == 7
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.tp_status_string(code).decode() == name
 
@@ -296,6 +296,59 @@ def test_lora_workspace_and_empty(lib):
     assert lib.tp_lora_workspace_size(4096, 65) == 0
     assert lo(lib, m=0, ws=0, wsb=0) == 0
     assert lo(lib, n=0, ws=0, wsb=0) == 0
+
+
+def ld(lib, x=A, xd=1, ldx=512, la=B, ad=1, lda=512, m=64, k=512, r=32, t=D, tb=64 * 64 * 4):
+    return lib.tp_lora_down(x, xd, ldx, la, ad, lda, m, k, r, t, tb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=300, ldx=304, lda=304), 3),
+    (dict(r=0), 2),
+    (dict(r=65), 2),
+    (dict(x=0), 1),
+    (dict(la=0), 1),
+    (dict(t=0), 1),
+    (dict(ldx=500), 4),
+    (dict(x=A + 1), 5),
+    (dict(t=D + 8), 5),
+    (dict(xd=2), 6),
+    (dict(ad=9), 6),
+    (dict(tb=64 * 64 * 4 - 4), 9),
+    (dict(t=A + 256), 10),             # t overlaps x
+])
+def test_lora_down_refusals(lib, kw, status):
+    assert ld(lib, **kw) == status, _err(lib)
+    assert _err(lib)
+
+
+def lq(lib, qa=A, ldqa=512, sa=B, q=B + 4096, ldq=512, sw=C, m=64, n=256, k=512, c=D, ldc=256, t=E,
+       lb=E + 65536, ldb=32, r=32, alpha=0.5, ws=0x20000000, wsb=1 << 26):
+    return lib.tp_qgemm_w8a8_prequantized_lora(qa, ldqa, sa, q, ldq, sw, m, n, k, c, ldc, t, lb, ldb, r, alpha,
+                                               ws or None, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=300, ldqa=304, ldq=304), 3),
+    (dict(r=0), 2),
+    (dict(r=65, ldb=72), 2),
+    (dict(t=0), 1),
+    (dict(lb=0), 1),
+    (dict(ldb=16), 4),                 # lora_b pitch below r
+    (dict(ldb=33), 5),                 # lora_b rows must be 16-byte aligned
+    (dict(t=E + 8), 5),
+    (dict(ldc=255), 4),
+    (dict(t=D + 64), 10),              # t overlaps c
+    (dict(lb=D + 128), 10),            # lora_b overlaps c
+])
+def test_w8a8_lora_refusals(lib, kw, status):
+    assert lq(lib, **kw) == status, _err(lib)
+    assert _err(lib)
+
+
+def test_w8a8_lora_empty(lib):
+    assert lq(lib, m=0, ws=0, wsb=0) == 0
+    assert lq(lib, n=0, ws=0, wsb=0) == 0
 
 
 # -------------------------------------------------------------- loader

@@ -15,7 +15,7 @@ import torch
 import int4_quantized_gemm_amd as tp
 import oracle
 import workloads as W
-from tests.gpu_util import announce, dev, f64, host
+from tests.gpu_util import announce, dev, f64, host, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -119,3 +119,33 @@ def test_lora_matrix_unit_views(cd, off, pad):
     _check(view, c, x, a, b, 0.6, bf16_out=cd == "bf16")
     assert torch.all(cbuf[0] == 4.0) and torch.all(cbuf[-1] == 4.0)
     assert torch.all(cbuf[:, :off] == 4.0) and torch.all(cbuf[:, off + n:] == 4.0)
+
+
+@pytest.mark.parametrize("m,n,k,r", [
+    (4096, 9216, 3072, 32),    # qkv at full size: the single-pass kernel, side path in its store
+    (4096, 9216, 3072, 64),
+    (2000, 5000, 512, 13),     # ragged M and N on the single-pass kernel, a partial lora_b vector
+    (512, 1024, 3072, 40),     # split K: product, then the standalone up half
+    (48, 3000, 1024, 7),       # few rows: product, then the standalone up half
+])
+def test_w8a8_lora_in_store(m, n, k, r):
+    """tp_lora_down + tp_qgemm_w8a8_prequantized_lora give the bits of
+    tp_qgemm_w8a8_prequantized followed by tp_lora_add (bf16 x, lora_a,
+    lora_b), and the side path stays inside the fp32 bound of the oracle's
+    (sampled rows, against the product alone)."""
+    d = dev()
+    announce("tp_qgemm_w8a8_prequantized_lora", m, n, k, r)
+    x = W.random_rows((m, k), seed=m + r, dtype="bf16")
+    _, a, b, _ = _lora_inputs(1, n, k, r, seed=n + r)
+    w = W.random_rows((n, k), seed=k + r, dtype="f32", scale=0.02)
+    xd, ad, bd = x.to(d), a.to(d), _padded_b(b, d)
+    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    qa, sa = tp.tp_quantize_rows_int8(xd, rotate=True)
+    base = tp.tp_qgemm_w8a8_prequantized(qa, sa, q, s)
+    sep = base.clone()
+    tp.tp_lora_add(sep, xd, ad, bd, 0.7)
+    t = tp.tp_lora_down(xd, ad)
+    fused = tp.tp_qgemm_w8a8_prequantized_lora(qa, sa, q, s, t, bd, 0.7)
+    assert torch.equal(fused, sep), f"{int((fused != sep).sum())} elements differ from product + tp_lora_add"
+    sel = sample_rows(m, 16, seed=r)
+    _check(fused[sel], base[sel], x[sel], a, b, 0.7)
