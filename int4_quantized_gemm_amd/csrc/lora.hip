@@ -166,23 +166,35 @@ __global__ __launch_bounds__(256) void k_lora_up_add(const float* __restrict__ t
 // in fp32, so bf16 MFMAs with fp32 sums keep the arithmetic above: fp32 sums,
 // C rounded once.
 
-// Down, bf16 X and lora_A: one block per 16 rows of X; its 8 waves split K in
-// eighths (k is a multiple of 256, so each eighth is whole 32-deep steps) and
-// their partial sums are added in LDS in wave order. Lane l feeds X row l % 16
-// and lora_A row 16 f + l % 16 (zero past r) with K chunk 8 (l / 16) of each
-// step.
+// Down, bf16 X and lora_A: one block per LDM_FM x 16 rows of X; its LDM_NW
+// waves split the K / 32 steps of 32 as evenly as whole steps allow (some
+// waves get none when k < 32 * LDM_NW) and their partial sums are added in
+// LDS in wave order. Lane l feeds
+// X rows 16 i + l % 16 and lora_A row 16 f + l % 16 (zero past r) with K chunk
+// 8 (l / 16) of each step.
+constexpr int LDM_FM = 1;  // 16-row fragments of X per block (2 and 4 were slower: fewer waves)
+constexpr int LDM_NW = 16;  // waves per block, each with 1 / LDM_NW of K (16: 15% faster than 8 at k = 12288)
+
 template <int R>
-__global__ __launch_bounds__(512) void k_lora_down_mfma(const uint16_t* __restrict__ x, int64_t ldx,
+__global__ __launch_bounds__(64 * LDM_NW) void k_lora_down_mfma(const uint16_t* __restrict__ x, int64_t ldx,
                                                         const uint16_t* __restrict__ a, int64_t lda, int M, int K,
                                                         int r, float* __restrict__ t) {
   constexpr int NF = R / 16;  // 16-column fragments of T
-  __shared__ __align__(16) float part[8][16][R];
+  constexpr int BR = 16 * LDM_FM;
+  __shared__ __align__(16) float part[LDM_NW][BR][R];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int m0 = blockIdx.x * 16;
-  const int kw = K / 8, kb = wave * kw;
-  const bool rowok = m0 + l16 < M;
-  const uint16_t* xrow = x + (int64_t)min(m0 + l16, M - 1) * ldx + kb + 8 * g4;
+  const int m0 = blockIdx.x * BR;
+  // This wave's whole 32-deep steps of K: [s0, s1) of the K / 32.
+  const int nk = K / 32, s0 = wave * nk / LDM_NW, s1 = (wave + 1) * nk / LDM_NW;
+  const int kb = s0 * 32, kw = (s1 - s0) * 32;
+  bool rowok[LDM_FM];
+  const uint16_t* xrow[LDM_FM];
+#pragma unroll
+  for (int i = 0; i < LDM_FM; ++i) {
+    rowok[i] = m0 + 16 * i + l16 < M;
+    xrow[i] = x + (int64_t)min(m0 + 16 * i + l16, M - 1) * ldx + kb + 8 * g4;
+  }
   const uint16_t* arow[NF];
   bool aok[NF];
 #pragma unroll
@@ -191,34 +203,42 @@ __global__ __launch_bounds__(512) void k_lora_down_mfma(const uint16_t* __restri
     aok[f] = j < r;
     arow[f] = a + (int64_t)min(j, r - 1) * lda + kb + 8 * g4;
   }
-  f32x4_t acc[NF];
+  f32x4_t acc[LDM_FM][NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < LDM_FM; ++i)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll 4
   for (int k = 0; k < kw; k += 32) {
-    const u32x4_t xv = rowok ? *reinterpret_cast<const u32x4_t*>(xrow + k) : zero;
+    u32x4_t xv[LDM_FM];
+#pragma unroll
+    for (int i = 0; i < LDM_FM; ++i) xv[i] = rowok[i] ? *reinterpret_cast<const u32x4_t*>(xrow[i] + k) : zero;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const u32x4_t av = aok[f] ? *reinterpret_cast<const u32x4_t*>(arow[f] + k) : zero;
-      acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
-                                                       __builtin_bit_cast(bf16x8_t, av), acc[f], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < LDM_FM; ++i)
+        acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[i]),
+                                                            __builtin_bit_cast(bf16x8_t, av), acc[i][f], 0, 0, 0);
     }
   }
-  // lane l holds rows 4 (l / 16) + v, column 16 f + l % 16
+  // lane l holds rows 16 i + 4 (l / 16) + v, column 16 f + l % 16
 #pragma unroll
-  for (int f = 0; f < NF; ++f)
+  for (int i = 0; i < LDM_FM; ++i)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) part[wave][4 * g4 + v][f * 16 + l16] = acc[f][v];
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part[wave][16 * i + 4 * g4 + v][f * 16 + l16] = acc[i][f][v];
   __syncthreads();
-  for (int e = threadIdx.x; e < 16 * LORA_RMAX; e += 512) {
+  for (int e = threadIdx.x; e < BR * LORA_RMAX; e += 64 * LDM_NW) {
     const int i = e / LORA_RMAX, j = e % LORA_RMAX;
     if (m0 + i >= M) continue;
     float sum = 0.f;
     if (j < R && j < r) {
       sum = part[0][i][j];
 #pragma unroll
-      for (int w = 1; w < 8; ++w) sum += part[w][i][j];
+      for (int w = 1; w < LDM_NW; ++w) sum += part[w][i][j];
     }
     t[(int64_t)(m0 + i) * LORA_RMAX + j] = sum;
   }
@@ -338,7 +358,7 @@ static hipError_t lora_down_r(const void* x, bool x_bf16, int64_t ldx, const voi
                      (int)k, (int)r, t)
   if (x_bf16) {
     if (a_bf16)
-      hipLaunchKernelGGL((k_lora_down_mfma<R>), dim3((unsigned)((m + 15) / 16)), dim3(512), 0, stream,
+      hipLaunchKernelGGL((k_lora_down_mfma<R>), dim3((unsigned)((m + 16 * LDM_FM - 1) / (16 * LDM_FM))), dim3(64 * LDM_NW), 0, stream,
                          (const uint16_t*)x, ldx, (const uint16_t*)a, lda, (int)m, (int)k, (int)r, t);
     else
       TP_DOWN(uint16_t, float);
