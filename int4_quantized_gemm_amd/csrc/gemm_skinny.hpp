@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void k_qgemm_skinny(const uint8_t* __restrict_
 #pragma unroll
           for (int j = 0; j < SK_FNW; ++j) {
             const uint32_t word = d == 0 ? w[j][t].x : d == 1 ? w[j][t].y : d == 2 ? w[j][t].z : w[j][t].w;
-            b[j] = pp_widen_i4x8(word);
+            b[j] = pp_widen_i4x8_x16(word, 0xF0F0F0F0u);  // 16 x code (exact)
           }
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void k_qgemm_skinny(const uint8_t* __restrict_
           for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < SK_FNW; ++j) {
-              tot[i][j] += sg[j] * acc[i][j];
+              tot[i][j] += (sg[j] * 0.0625f) * acc[i][j];  // acc holds 16 x the sums
               acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
         }
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(GV_NW * 64) void k_qgemv(const uint8_t* __restrict_
         for (int d = 0; d < 4; ++d) {
           const uint32_t word = d == 0 ? st.w[t].x : d == 1 ? st.w[t].y : d == 2 ? st.w[t].z : st.w[t].w;
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, st.a[4 * t + d]),
-                                                        pp_widen_i4x8(word), acc, 0, 0, 0);
+                                                        pp_widen_i4x8_x16(word, 0xF0F0F0F0u), acc, 0, 0, 0);
         }
     }
   };
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(GV_NW * 64) void k_qgemv(const uint8_t* __restrict_
         compute(ring[d]);
         if (g + d + 2 < ge) load(ring[d], g + d + 2);
         if constexpr (KIND == GEMM_W4) {
-          tot += sg * acc;
+          tot += (sg * 0.0625f) * acc;  // acc holds 16 x the sums (16 x code, exact)
           acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
       }
