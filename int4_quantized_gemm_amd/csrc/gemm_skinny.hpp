@@ -291,9 +291,9 @@ constexpr int GV_MAX_M = 8;  // rows up to which k_qgemv is used (measured: from
 constexpr int GV_LDS_MAX = 48 * 1024;  // activation bytes (M rows x K) staged in LDS when they fit (with
                                        // the 8 KB of partial sums, within the default 64 KB a block)
 
-// ALDS (W8A8): the block first copies the M activation rows into LDS
-// (dynamic shared memory, M * K bytes) and the waves read their fragments
-// there. Every lane of a 16-lane group needs the same activation bytes (rows
+// ALDS (W8A8, W4): the block first copies the M activation rows into LDS
+// (dynamic shared memory, M * K * AB bytes) and the waves read their
+// fragments there. Every lane of a 16-lane group needs the same activation bytes (rows
 // past M are clamped copies), so read from global memory the fragments cost as
 // many load instructions as the weights; from LDS they are broadcast reads.
 template <int KIND, bool OUT_BF16, bool ACC_OUT, bool ALDS>
@@ -377,9 +377,16 @@ __global__ __launch_bounds__(GV_NW * 64) void k_qgemv(const uint8_t* __restrict_
     }
   };
 
-  Stage ring[2];
-  if (gb < ge) load(ring[0], gb);
-  if (gb + 1 < ge) load(ring[1], gb + 1);
+  // Groups of weight codes in flight per wave. W4 with the activations in
+  // LDS: a stage is only its 32 bytes of codes a lane, so all 6 groups of a
+  // 48-group K split 8 ways are loaded ahead (M = 1, 3072 x 12288: 10.7 ->
+  // 9.9 us). For W8A8 the extra registers cost a resident block per CU and
+  // were slower (gate+up 14.8 -> 17.5 us).
+  constexpr int DEPTH = ALDS && KIND == GEMM_W4 ? 6 : 2;
+  Stage ring[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (gb + d < ge) load(ring[d], gb + d);
   if constexpr (ALDS) {
     // The M activation rows into LDS, 16 bytes per thread per step (the
     // weight loads above are already in flight).
@@ -390,15 +397,15 @@ __global__ __launch_bounds__(GV_NW * 64) void k_qgemv(const uint8_t* __restrict_
     }
     __syncthreads();
   }
-  for (int g = gb; g < ge; g += 2) {
+  for (int g = gb; g < ge; g += DEPTH) {
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
+    for (int d = 0; d < DEPTH; ++d) {
       if (g + d < ge) {
         float sg = 0.f;
         if constexpr (KIND == GEMM_W4) sg = sw[(int64_t)min(ncol, N - 1) * G + g + d];
         if constexpr (ALDS) load_a_lds(ring[d], g + d);
         compute(ring[d]);
-        if (g + d + 2 < ge) load(ring[d], g + d + 2);
+        if (g + d + DEPTH < ge) load(ring[d], g + d + DEPTH);
         if constexpr (KIND == GEMM_W4) {
           tot += (sg * 0.0625f) * acc;  // acc holds 16 x the sums (16 x code, exact)
           acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -445,8 +452,8 @@ static hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
   const dim3 grid((unsigned)((g.n + 15) / 16)), block(GV_NW * 64);
   const int64_t act_bytes = g.m * g.k * (KIND == GEMM_W8A8 ? 1 : 2);
   // Staging measured at M = 1: W8A8 qkv 10.3 -> 8.3 us and gate+up 18.3 -> 14.7 us;
-  // no gain for the bf16 activations of W8 and W4 (kept on direct loads).
-  const bool alds = KIND == GEMM_W8A8 && act_bytes <= GV_LDS_MAX;
+  // W4 (with the deeper prefetch it allows) 10.7 -> 9.9 us; no gain for W8.
+  const bool alds = (KIND == GEMM_W8A8 || KIND == GEMM_W4) && act_bytes <= GV_LDS_MAX;
 #define TP_LAUNCH_GV(OB, AO, AL)                                                                              \
   hipLaunchKernelGGL((k_qgemv<KIND, OB, AO, AL>), grid, block, AL ? (size_t)act_bytes : 0, stream, a, lda_bytes, \
                      b, g.ldb, g.w_scales, g.a_scales, (int)g.m, (int)g.n, (int)g.k, g.c, g.ldc, g.acc_out,   \
