@@ -28,6 +28,8 @@
 // The activation fragment of the same MFMA reads those K indices from LDS.
 #pragma once
 
+#include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -47,12 +49,13 @@ struct SkTraits {
 // bit 2 is set (see the activation staging in k_qgemm_skinny).
 __device__ __forceinline__ int sk_swz(int r) { return r ^ ((r << 1) & 8); }
 
-constexpr int SK_FNW = 2;               // 16-row weight fragments per wave
-constexpr int SK_BN = 4 * 16 * SK_FNW;  // weight rows per block (four waves)
+constexpr int SK_NW = 4;                    // waves per block
+constexpr int SK_FNW = 2;                   // 16-row weight fragments per wave
+constexpr int SK_BN = SK_NW * 16 * SK_FNW;  // weight rows per block
 constexpr int SK_DG = 2;                // 256-groups of codes in flight per wave
 
 template <int KIND, int FM, bool OUT_BF16, bool ACC_OUT, bool PARTIAL>
-__global__ __launch_bounds__(256) void k_qgemm_skinny(const uint8_t* __restrict__ A, int64_t lda_bytes,
+__global__ __launch_bounds__(SK_NW * 64) void k_qgemm_skinny(const uint8_t* __restrict__ A, int64_t lda_bytes,
                                                       const uint8_t* __restrict__ B, int64_t ldb,
                                                       const float* __restrict__ sw, const float* __restrict__ sa,
                                                       int M, int N, int K, void* __restrict__ C, int64_t ldc,
@@ -94,9 +97,6 @@ __global__ __launch_bounds__(256) void k_qgemm_skinny(const uint8_t* __restrict_
       for (int t = 0; t < T::LPG; ++t)
         dst[j][t] = *reinterpret_cast<const u32x4_t*>(wrow[j] + (int64_t)gi * T::WBG + 64 * t);
   };
-#pragma unroll
-  for (int d = 0; d < SK_DG; ++d)
-    if (d < ng) load_group(wr[d], d);
 
   // Activation rows m0 .. m0+MR-1 (clamped to M-1: rows past M only feed
   // output rows that are never stored), K range of this split, into LDS with
@@ -108,27 +108,39 @@ __global__ __launch_bounds__(256) void k_qgemm_skinny(const uint8_t* __restrict_
   // {0-3, 12-15} of one lane group with rows {4-11} of the next in one pass
   // (gfx950, measured): sk_swz sends the first set to bank groups 0-7 and the
   // second to 8-15 for all three steps. Each wave instruction fills 64
-  // consecutive slots.
+  // consecutive slots; the total is a multiple of 256 slots, so every wave
+  // instruction is whole.
   const int cpr = ng * 256 * T::AB / 16;  // 16-byte columns per row, a multiple of 16
   {
     const int total = MR * cpr;  // a multiple of 256
     const uint8_t* abase = A + (int64_t)g0 * 256 * T::AB;
     const int s = wave * 64 + lane;
     int r = s / cpr, p = s - r * cpr;
-    for (int s0 = wave * 64; s0 < total; s0 += 256) {
+    for (int s0 = wave * 64; s0 < total; s0 += SK_NW * 64) {
       const int c = p ^ sk_swz(r & 15);
       const int m = min(m0 + r, M - 1);
       __builtin_amdgcn_global_load_lds((const void*)(abase + (int64_t)m * lda_bytes + c * 16),
                                        (lds_void_t*)(sk_lds + s0 * 16), 16, 0, 0);
-      p += 256;
+      p += SK_NW * 64;
       while (p >= cpr) {
         p -= cpr;
         ++r;
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(0));
-  __syncthreads();
+  // The first weight groups go out after the activation stage, so the wait
+  // for the stage leaves them in flight (a wave's loads complete in issue
+  // order), and each group's products start as soon as its own codes land.
+#pragma unroll
+  for (int d = 0; d < SK_DG; ++d)
+    if (d < ng) load_group(wr[d], d);
+  constexpr int GL = SK_FNW * T::LPG;  // loads per weight group
+  static_assert(SK_DG == 2 && 2 * GL < 64, "vmcnt range");
+  if (ng >= 2)
+    __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(2 * GL));
+  else
+    __builtin_amdgcn_s_waitcnt(VMCNT_ENCODE(GL));
+  barrier_only();  // no fence: it would wait for the weight loads too
 
   acc_t acc[FM][SK_FNW];
   f32x4_t tot[KIND == GEMM_W4 ? FM : 1][SK_FNW];
@@ -476,29 +488,40 @@ static hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
 }
 
 // Sum of the split partials in split order, then the epilogue. One thread per
-// output element; blockIdx.y is the row.
+// output element; blockIdx.y is the row. The scales and each run of up to
+// eight partials are loaded before any of them is added, so the loads are in
+// flight together instead of each waiting on the previous add (the additions
+// themselves keep split order).
 template <int KIND, bool OUT_BF16, bool ACC_OUT>
 __global__ __launch_bounds__(256) void k_qgemm_reduce(const void* __restrict__ part, int splits, int M, int N,
                                                       const float* __restrict__ sw, const float* __restrict__ sa,
                                                       void* __restrict__ C, int64_t ldc,
                                                       int32_t* __restrict__ acc_out, int64_t ld_acc) {
+  constexpr int RUN = 8;
   const int n = blockIdx.x * 256 + threadIdx.x;
   const int m = blockIdx.y;
   if (n >= N) return;
   const int64_t plane = (int64_t)M * N;
   const int64_t off = (int64_t)m * N + n;
+  const float scol = (KIND == GEMM_W8A8 || KIND == GEMM_W8) ? sw[n] : 1.f;
+  const float srow = (KIND == GEMM_W8A8 || KIND == GEMM_W4A8) ? sa[m] : 1.f;
+  typedef typename std::conditional<KIND == GEMM_W8A8, int32_t, float>::type part_t;
+  const part_t* p = reinterpret_cast<const part_t*>(part) + off;
+  part_t s = p[0];
+  for (int sp0 = 1; sp0 < splits; sp0 += RUN) {
+    part_t v[RUN];
+#pragma unroll
+    for (int u = 0; u < RUN; ++u) v[u] = sp0 + u < splits ? p[(sp0 + u) * plane] : part_t(0);
+#pragma unroll
+    for (int u = 0; u < RUN; ++u)
+      if (sp0 + u < splits) s += v[u];
+  }
   float y;
   if constexpr (KIND == GEMM_W8A8) {
-    const int32_t* p = reinterpret_cast<const int32_t*>(part);
-    int32_t s = p[off];
-    for (int sp = 1; sp < splits; ++sp) s += p[sp * plane + off];
     if constexpr (ACC_OUT) acc_out[(int64_t)m * ld_acc + n] = s;
-    y = ((float)s * sa[m]) * sw[n];
+    y = ((float)s * srow) * scol;
   } else {
-    const float* p = reinterpret_cast<const float*>(part);
-    float s = p[off];
-    for (int sp = 1; sp < splits; ++sp) s += p[sp * plane + off];
-    y = KIND == GEMM_W8 ? s * sw[n] : (KIND == GEMM_W4A8 ? s * sa[m] : s);
+    y = KIND == GEMM_W8 ? s * scol : (KIND == GEMM_W4A8 ? s * srow : s);
   }
   if constexpr (OUT_BF16)
     reinterpret_cast<__bf16*>(C)[(int64_t)m * ldc + n] = (__bf16)y;
@@ -519,39 +542,75 @@ struct SkPlan {
 };
 
 constexpr int SK_MAX_M = 64;           // rows up to which the small-M path is used
-constexpr int SK_TARGET_BLOCKS = 512;  // two blocks per CU
 constexpr int SK_MAX_LDS = 64 * 1024;  // activation stage per block (the default dynamic-LDS limit)
+constexpr int SK_CUS = 256;            // compute units of the device the plan is tuned for
 
+// Blocks (one wave per SIMD each) that one CU holds at once as far as the
+// register use of the built kernels goes, by kind and fm (1, 2, 4); only the
+// plan's speed depends on these.
+inline int sk_reg_blocks(int kind, int fm) {
+  const int i = fm == 1 ? 0 : (fm == 2 ? 1 : 2);
+  static const int w8[3] = {4, 3, 2}, w4[3] = {5, 4, 3}, w8a8[3] = {4, 4, 2};
+  return kind == GEMM_W8 ? w8[i] : (kind == GEMM_W4 ? w4[i] : w8a8[i]);
+}
+
+// Estimated time (us) of one small-M plan, fitted to measurements of the
+// split-K kernel on MI355X (cold weights, 16 to 64 rows, K 3072 and 12288,
+// N 3072 to 24576). The kernel takes the largest of three floors: the weights
+// at 7 TB/s; the busiest CU streaming its blocks' codes at about 40 GB/s (a
+// block's loads are latency-bound); and, per round of resident blocks, about
+// 1 us of load latency per two groups plus the products (0.25 us per group
+// and 16 rows for W8 and W4, 0.075 for W8A8). Splits add their partial sums
+// (written and read once) and the reduction launch.
+inline double sk_plan_cost_us(int kind, int64_t m, int64_t n, int64_t k, int fm, int64_t mb, int64_t nb,
+                              int64_t gps, int64_t splits, int lds) {
+  const double wbytes = (double)n * (double)k * (kind == GEMM_W4 ? 0.5 : 1.0);
+  const double blocks = (double)(nb * mb * splits);
+  const int per_cu = std::min(std::min(163840 / lds, sk_reg_blocks(kind, fm)), 8);
+  const double rounds = std::ceil(blocks / (SK_CUS * per_cu));
+  const double busiest = std::ceil(blocks / SK_CUS) * (wbytes * (double)mb / blocks);
+  const double mma = (kind == GEMM_W8A8 ? 0.075 : 0.25) * fm * (double)gps;
+  const double tblock = 1.0 * (double)((gps + 1) / 2) + mma;
+  const double part = splits > 1 ? (double)splits * (double)m * (double)n * 4.0 : 0.0;
+  return std::max(std::max(wbytes / 7.0e6, busiest / 4.0e4), rounds * tblock) + 2.0 * part / 7.0e6 +
+         (splits > 1 ? 1.0 : 0.0);
+}
+
+// The plan with the lowest estimate over fm (up to the fragments M needs) and
+// every balanced split of the 256-groups whose activation stage fits in LDS;
+// ties go to fewer splits. A pure function of the shape, so the workspace size
+// query and the launch agree.
 inline bool skinny_plan(int kind, int64_t m, int64_t n, int64_t k, SkPlan* p) {
   if (kind == GEMM_W4A8 || m < 1 || m > SK_MAX_M || n < 1 || k < 256) return false;
   if (m <= GV_MAX_M) {
     *p = SkPlan{true, 1, 1, (int)((n + 15) / 16), 1, (int)(k / 256), 0};
     return (n + 15) / 16 <= INT32_MAX;
   }
-  const int fm = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-  const int mr = 16 * fm;
   const int ab = kind == GEMM_W8A8 ? 1 : 2;
   const int64_t G = k / 256;
-  const int64_t mb = (m + mr - 1) / mr;
   const int64_t nb = (n + SK_BN - 1) / SK_BN;
-  const int64_t gmax = SK_MAX_LDS / mr / (256 * ab);
-  const int64_t base = nb * mb;
-  if (gmax < 1 || base > INT32_MAX) return false;
-  int64_t splits = (SK_TARGET_BLOCKS + base - 1) / base;
-  if (splits > G) splits = G;
-  if (splits < 1) splits = 1;
-  int64_t gps = (G + splits - 1) / splits;
-  if (gps > gmax) gps = gmax;
-  splits = (G + gps - 1) / gps;
-  if (base * splits > INT32_MAX) return false;
-  p->gemv = false;
-  p->fm = fm;
-  p->mb = (int)mb;
-  p->nb = (int)nb;
-  p->splits = (int)splits;
-  p->gps = (int)gps;
-  p->lds = mr * (int)(gps * 256 * ab);
-  return true;
+  const int fm_need = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+  bool found = false;
+  double best = 0.0;
+  for (int fm = 1; fm <= fm_need; fm *= 2) {
+    const int mr = 16 * fm;
+    const int64_t mb = (m + mr - 1) / mr;
+    for (int64_t sp = 1; sp <= G; ++sp) {
+      const int64_t gps = (G + sp - 1) / sp;
+      const int64_t splits = (G + gps - 1) / gps;
+      if (splits != sp) continue;  // the same split as a smaller count
+      if ((int64_t)mr * gps * 256 * ab > SK_MAX_LDS) continue;
+      if (nb * mb * splits > INT32_MAX) continue;
+      const int lds = mr * (int)(gps * 256 * ab);
+      const double c = sk_plan_cost_us(kind, m, n, k, fm, mb, nb, gps, splits, lds);
+      if (!found || c < best) {
+        found = true;
+        best = c;
+        *p = SkPlan{false, fm, (int)mb, (int)nb, (int)splits, (int)gps, lds};
+      }
+    }
+  }
+  return found;
 }
 
 template <int KIND, int FM>
@@ -559,7 +618,7 @@ static hipError_t launch_skinny_fm(const GemmArgs& g, const SkPlan& p, hipStream
   const int64_t lda_bytes = g.lda * (KIND == GEMM_W8A8 ? 1 : 2);
   const uint8_t* a = (const uint8_t*)g.a;
   const uint8_t* b = (const uint8_t*)g.b;
-  const dim3 grid((unsigned)(p.nb * p.splits * p.mb)), block(256);
+  const dim3 grid((unsigned)(p.nb * p.splits * p.mb)), block(SK_NW * 64);
   const bool split = p.splits > 1;
 #define TP_LAUNCH_SK(OB, AO, PA)                                                                                 \
   hipLaunchKernelGGL((k_qgemm_skinny<KIND, FM, OB, AO, PA>), grid, block, p.lds, stream, a, lda_bytes, b, g.ldb, \

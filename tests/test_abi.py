@@ -214,7 +214,8 @@ def w8a8(lib, a=A, ad=1, lda=512, flags=1, q=B, ldq=512, s=C, m=64, n=256, k=512
     (dict(c=B), 10),                                 # c overlaps q
     (dict(flags=-1), 11),
     (dict(qa=0x30000000, sa=0x30000000 + 64 * 512 - 4), 10),
-    (dict(m=40, qa=0x30000000, sa=0x38000000, ws=0, wsb=0), 9),   # split-K partial sums still need room
+    (dict(m=40, k=3072, lda=3072, ldq=3072, qa=0x30000000, sa=0x38000000, ws=0, wsb=0), 9),  # split-K partials
+                                                                                           # still need room
 ])
 def test_w8a8_refusals(lib, kw, status):
     assert w8a8(lib, **kw) == status, _err(lib)
@@ -225,15 +226,21 @@ def test_w8a8_own_codes_need_no_workspace(lib):
 
 
 def test_small_m_workspace_refusals(lib):
-    # a pre-rotated product with 17..64 rows still needs room for its split-K
-    # partial sums; up to 8 rows it needs none (single-launch kernel)
-    assert w8(lib, flags=0, m=40, ws=0, wsb=0) == 9
-    need = lib.tp_workspace_size(1, 40, 256, 512, 0)
+    # a pre-rotated product with 9..64 rows that is split over K still needs
+    # room for its partial sums; up to 8 rows it needs none (single-launch
+    # kernel), and neither does a plan with one split
+    big = dict(flags=0, m=40, k=3072, lda=3072, ldq=3072)
+    assert w8(lib, ws=0, wsb=0, **big) == 9
+    need = lib.tp_workspace_size(1, 40, 256, 3072, 0)
     assert need > 0
-    assert w8(lib, flags=0, m=40, wsb=need - 1) == 9
-    assert w8(lib, flags=0, m=40, ws=E + 8, wsb=need) == 5
+    assert w8(lib, wsb=need - 1, **big) == 9
+    assert w8(lib, ws=E + 8, wsb=need, **big) == 5
+    assert lib.tp_workspace_size(1, 40, 256, 512, 0) == 0
     assert lib.tp_workspace_size(1, 8, 12288, 3072, 0) == 0
     assert lib.tp_workspace_size(4, 1, 24576, 3072, 0) == 0
+
+
+K3 = dict(k=3072, ldqa=3072, ldq=3072)  # a 64 x 256 x 3072 product is split over K
 
 
 def pq(lib, qa=A, ldqa=512, sa=C, q=B, ldq=512, s=C + 4096, m=64, n=256, k=512, c=D, cd=0, ldc=256, acc=0, ld_acc=0,
@@ -243,11 +250,11 @@ def pq(lib, qa=A, ldqa=512, sa=C, q=B, ldq=512, s=C + 4096, m=64, n=256, k=512, 
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(ws=0, wsb=0), 9),            # m <= 64: split-K partial sums need a workspace
-    (dict(wsb=1000), 9),
-    (dict(ws=E + 4), 5),
-    (dict(ws=A), 10),                  # workspace overlaps qa
-    (dict(ws=D), 10),                  # workspace overlaps c
+    (dict(ws=0, wsb=0, **K3), 9),      # m <= 64, K = 3072: split-K partial sums need a workspace
+    (dict(wsb=1000, **K3), 9),
+    (dict(ws=E + 4, **K3), 5),
+    (dict(ws=A, **K3), 10),            # workspace overlaps qa
+    (dict(ws=D, **K3), 10),            # workspace overlaps c
     (dict(k=300, ldqa=512, ldq=512), 3),
     (dict(cd=3), 6),
 ])

@@ -440,10 +440,11 @@ def _small_m_case(kind, wl, rows=None, out_dtype=torch.float32):
 @pytest.mark.parametrize("kind", ["w8", "w4", "w8a8"])
 @pytest.mark.parametrize("m,n,k", [(1, 300, 512), (5, 1000, 2560), (8, 4100, 3840), (9, 333, 1280),
                                    (16, 129, 256), (17, 777, 1536), (33, 4000, 768), (64, 515, 3072),
-                                   (64, 128, 12288), (3, 20, 12288)])
+                                   (64, 128, 12288), (3, 20, 12288), (40, 2000, 3072), (57, 3000, 12288)])
 def test_small_m_ragged(kind, m, n, k):
     """Few-row products: split-K with several 256-groups per split, ragged N,
-    M not a multiple of 16, a single 256-group (no split)."""
+    M not a multiple of 16, a single 256-group (no split), and plans with
+    several blocks along M whose last block is partly past M."""
     announce("small-m", kind, m, n, k)
     wl = W.TINY.with_(name=f"smallm_{m}_{n}_{k}", m=m, n=n, k=k, seed=m * 31 + n + k, act_outliers=2,
                       w_outliers=2, path=kind)
