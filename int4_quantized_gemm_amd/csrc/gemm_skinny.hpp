@@ -127,6 +127,19 @@ __global__ __launch_bounds__(SK_NW * 64) void k_qgemm_skinny(const uint8_t* __re
         ++r;
       }
     }
+    // W4: the split's group scales of the block's SK_BN weight rows join the
+    // stage (slot col * ng + g after the activations, one dword per lane), so
+    // no group waits on a scale load of its own. SK_BN * ng is a multiple of
+    // 64, so every wave instruction is whole.
+    if constexpr (KIND == GEMM_W4) {
+      const int nsc = SK_BN * ng;
+      for (int s0 = wave * 64; s0 < nsc; s0 += SK_NW * 64) {
+        const int e = s0 + lane, col = e / ng, gg = e - col * ng;
+        const int n = min(nbi * SK_BN + col, N - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(sw + (int64_t)n * G + g0 + gg),
+                                         (lds_void_t*)(sk_lds + (int64_t)total * 16 + s0 * 4), 4, 0, 0);
+      }
+    }
   }
   // The first weight groups go out after the activation stage, so the wait
   // for the stage leaves them in flight (a wave's loads complete in issue
@@ -229,8 +242,9 @@ __global__ __launch_bounds__(SK_NW * 64) void k_qgemm_skinny(const uint8_t* __re
       if (gi < ng) {
         float sg[SK_FNW];
         if constexpr (KIND == GEMM_W4) {
+          const float* ssc = reinterpret_cast<const float*>(sk_lds + MR * cpr * 16);
 #pragma unroll
-          for (int j = 0; j < SK_FNW; ++j) sg[j] = sw[(int64_t)min(ncol[j], N - 1) * G + g0 + gi];
+          for (int j = 0; j < SK_FNW; ++j) sg[j] = ssc[(ncol[j] - nbi * SK_BN) * ng + gi];
         }
         compute_group(wr[d], gi);
         if (gi + SK_DG < ng) load_group(wr[d], gi + SK_DG);
@@ -290,14 +304,21 @@ __global__ __launch_bounds__(SK_NW * 64) void k_qgemm_skinny(const uint8_t* __re
 // ------------------------------------------------------- M <= GV_MAX_M rows
 // One activation fragment (rows 0..15, rows past M clamped to M-1: they only
 // feed output rows that are never stored). A block owns 16 weight rows and the
-// whole K range; its GV_NW waves split K by 256-groups (contiguous ranges), so
+// whole K range; its waves split K by 256-groups (contiguous ranges), so
 // each weight byte is read once and every wave streams two groups ahead. The
 // activation fragments come straight from global memory (the same few rows are
 // read by every block, so they stay in L2); their K order is the weights' (see
 // the lane layout above). The waves' partial sums are added in LDS in wave
 // order (fixed, so the result does not depend on timing) and wave 0 applies the
 // epilogue. No workspace, one launch.
-constexpr int GV_NW = 8;     // waves per block
+// Waves per block. W8 (about 120 VGPRs a lane without the activation stage)
+// keeps all blocks of a 12288-row weight resident only with four waves a block
+// (M = 1: 11.2 -> 10.9 us, M = 8: 14.8 -> 12.8 us); W4 and W8A8 are faster
+// with eight (W4 at M = 1: 10.3 us with eight, 12.9 with four).
+template <int KIND>
+constexpr int gv_waves() {
+  return KIND == GEMM_W8 ? 4 : 8;
+}
 constexpr int GV_MAX_M = 8;  // rows up to which k_qgemv is used (measured: from 16 rows on, the
                              // split-K kernel's shared activation tile wins)
 constexpr int GV_LDS_MAX = 48 * 1024;  // activation bytes (M rows x K) staged in LDS when they fit (with
@@ -309,7 +330,7 @@ constexpr int GV_LDS_MAX = 48 * 1024;  // activation bytes (M rows x K) staged i
 // past M are clamped copies), so read from global memory the fragments cost as
 // many load instructions as the weights; from LDS they are broadcast reads.
 template <int KIND, bool OUT_BF16, bool ACC_OUT, bool ALDS>
-__global__ __launch_bounds__(GV_NW * 64) void k_qgemv(const uint8_t* __restrict__ A, int64_t lda_bytes,
+__global__ __launch_bounds__(gv_waves<KIND>() * 64) void k_qgemv(const uint8_t* __restrict__ A, int64_t lda_bytes,
                                                       const uint8_t* __restrict__ B, int64_t ldb,
                                                       const float* __restrict__ sw, const float* __restrict__ sa,
                                                       int M, int N, int K, void* __restrict__ C, int64_t ldc,
@@ -318,6 +339,7 @@ __global__ __launch_bounds__(GV_NW * 64) void k_qgemv(const uint8_t* __restrict_
   constexpr bool I8 = KIND == GEMM_W8A8;
   constexpr int ALD = I8 ? 4 : 8;  // 16-byte activation loads per lane per group
   using acc_t = typename std::conditional<I8, i32x4_t, f32x4_t>::type;
+  constexpr int GV_NW = gv_waves<KIND>();
   __shared__ __align__(16) uint8_t red[GV_NW][64][16];
   extern __shared__ __align__(16) uint8_t gv_act[];
 
@@ -461,7 +483,7 @@ static hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream) {
   const int64_t lda_bytes = g.lda * (KIND == GEMM_W8A8 ? 1 : 2);
   const uint8_t* a = (const uint8_t*)g.a;
   const uint8_t* b = (const uint8_t*)g.b;
-  const dim3 grid((unsigned)((g.n + 15) / 16)), block(GV_NW * 64);
+  const dim3 grid((unsigned)((g.n + 15) / 16)), block(gv_waves<KIND>() * 64);
   const int64_t act_bytes = g.m * g.k * (KIND == GEMM_W8A8 ? 1 : 2);
   // Staging measured at M = 1: W8A8 qkv 10.3 -> 8.3 us and gate+up 18.3 -> 14.7 us;
   // W4 (with the deeper prefetch it allows) 10.7 -> 9.9 us; no gain for W8.
@@ -599,9 +621,10 @@ inline bool skinny_plan(int kind, int64_t m, int64_t n, int64_t k, SkPlan* p) {
       const int64_t gps = (G + sp - 1) / sp;
       const int64_t splits = (G + gps - 1) / gps;
       if (splits != sp) continue;  // the same split as a smaller count
-      if ((int64_t)mr * gps * 256 * ab > SK_MAX_LDS) continue;
+      const int64_t lds64 = (int64_t)mr * gps * 256 * ab + (kind == GEMM_W4 ? (int64_t)SK_BN * gps * 4 : 0);
+      if (lds64 > SK_MAX_LDS) continue;
       if (nb * mb * splits > INT32_MAX) continue;
-      const int lds = mr * (int)(gps * 256 * ab);
+      const int lds = (int)lds64;
       const double c = sk_plan_cost_us(kind, m, n, k, fm, mb, nb, gps, splits, lds);
       if (!found || c < best) {
         found = true;
