@@ -143,7 +143,7 @@ __global__ __launch_bounds__(SK_NW * 64) void k_qgemm_skinny(const uint8_t* __re
   }
   // The first weight groups go out after the activation stage, so the wait
   // for the stage leaves them in flight (a wave's loads complete in issue
-  // order), and each group's products start as soon as its own codes land.
+  // order) until the first products need them.
 #pragma unroll
   for (int d = 0; d < SK_DG; ++d)
     if (d < ng) load_group(wr[d], d);

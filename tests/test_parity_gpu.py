@@ -597,3 +597,27 @@ def test_refusal_reaches_python():
     with pytest.raises(tp.TPError) as e:
         tp.tp_hadamard_rotate_rows(x)
     assert e.value.status_name == "TP_ERR_K_NOT_MULTIPLE_OF_256"
+
+
+@pytest.mark.parametrize("kind", ["w8", "w4"])
+@pytest.mark.parametrize("m,n,k,dt", [(1, 300, 512, "f32"), (8, 1000, 3072, "bf16"), (3, 20, 12288, "f32"),
+                                      (9, 333, 1280, "f32"), (16, 4100, 3072, "bf16"), (40, 2000, 3072, "f32"),
+                                      (64, 515, 12288, "bf16"), (5, 700, 12288, "bf16")])
+def test_small_m_rotation_matches_two_step(kind, m, n, k, dt):
+    """Few rows with the rotation requested (fp32 and bf16 operands, GEMV and
+    split-K plans): the bytes of rotating first to bf16 and multiplying the
+    rotated operand."""
+    d = dev()
+    announce("small-m rotation", kind, m, n, k, dt)
+    g = torch.Generator().manual_seed(m * 7 + n + k)
+    x = torch.randn((m, k), generator=g, dtype=torch.float64)
+    x[:, :: max(1, k // 13)] *= 30.0
+    x = x.to(torch.float32 if dt == "f32" else torch.bfloat16).to(d)
+    w = (torch.randn((n, k), generator=g, dtype=torch.float64) * 0.02).to(torch.float32).to(d)
+    q, s = tp.tp_rotate_quantize_weights(w, bits=4 if kind == "w4" else 8)
+    fn = tp.tp_qgemm_w8 if kind == "w8" else tp.tp_qgemm_w4
+    for out in (torch.bfloat16, torch.float32):
+        y1 = fn(x, q, s, rotate=True, out_dtype=out)
+        xr = tp.tp_hadamard_rotate_rows(x, out_dtype=torch.bfloat16)
+        y2 = fn(xr, q, s, rotate=False, out_dtype=out)
+        assert torch.equal(y1, y2), f"{int((y1 != y2).sum())} outputs differ from rotate-then-multiply"
