@@ -503,3 +503,18 @@ def test_binding_refuses_cpu_tensors():
     import int4_quantized_gemm_amd as tp
     with pytest.raises(ValueError):
         tp.tp_hadamard_rotate_rows(torch.zeros(4, 256))
+
+
+def test_small_m_plan_workspace_properties(lib):
+    """The 9..64-row plan (fragment height, groups per split) is a pure
+    function of the shape: repeated queries agree, and a split plan asks for
+    whole planes of M x N 4-byte partial sums, at most one per 256-group."""
+    import random
+    rnd = random.Random(5)
+    for _ in range(400):
+        m, n, k = rnd.randint(9, 64), rnd.randint(1, 30000), 256 * rnd.randint(1, 64)
+        for op in (1, 2, 4):  # W8, W4 pre-rotated; W8A8 pre-quantized
+            a = lib.tp_workspace_size(op, m, n, k, 0)
+            assert a == lib.tp_workspace_size(op, m, n, k, 0)
+            assert a % (m * n * 4) == 0, (op, m, n, k, a)
+            assert a // (m * n * 4) <= k // 256, (op, m, n, k, a)
