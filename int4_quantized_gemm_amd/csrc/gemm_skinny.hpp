@@ -551,6 +551,57 @@ __global__ __launch_bounds__(256) void k_qgemm_reduce(const void* __restrict__ p
     reinterpret_cast<float*>(C)[(int64_t)m * ldc + n] = y;
 }
 
+// The same sums and epilogue, four consecutive outputs a thread: 16-byte
+// partial loads and whole-vector stores (used when N, the output pitches and
+// the base addresses allow them). Each output adds its splits in split order
+// and is rounded exactly as in k_qgemm_reduce.
+template <int KIND, bool OUT_BF16, bool ACC_OUT>
+__global__ __launch_bounds__(256) void k_qgemm_reduce4(const void* __restrict__ part, int splits, int M, int N,
+                                                       const float* __restrict__ sw, const float* __restrict__ sa,
+                                                       void* __restrict__ C, int64_t ldc,
+                                                       int32_t* __restrict__ acc_out, int64_t ld_acc) {
+  constexpr int RUN = 8;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int m = blockIdx.y;
+  if (n >= N) return;
+  const int64_t plane = (int64_t)M * N;
+  const int64_t off = (int64_t)m * N + n;
+  float scol[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) scol[e] = (KIND == GEMM_W8A8 || KIND == GEMM_W8) ? sw[n + e] : 1.f;
+  const float srow = (KIND == GEMM_W8A8 || KIND == GEMM_W4A8) ? sa[m] : 1.f;
+  typedef typename std::conditional<KIND == GEMM_W8A8, i32x4_t, f32x4_t>::type vec_t;
+  const vec_t* p = reinterpret_cast<const vec_t*>(reinterpret_cast<const typename std::conditional<
+      KIND == GEMM_W8A8, int32_t, float>::type*>(part) + off);
+  vec_t s = p[0];
+  for (int sp0 = 1; sp0 < splits; sp0 += RUN) {
+    vec_t v[RUN];
+#pragma unroll
+    for (int u = 0; u < RUN; ++u) v[u] = sp0 + u < splits ? p[(sp0 + u) * (plane / 4)] : vec_t{};
+#pragma unroll
+    for (int u = 0; u < RUN; ++u)
+      if (sp0 + u < splits) s += v[u];
+  }
+  float y[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (KIND == GEMM_W8A8)
+      y[e] = ((float)s[e] * srow) * scol[e];
+    else
+      y[e] = KIND == GEMM_W8 ? s[e] * scol[e] : (KIND == GEMM_W4A8 ? s[e] * srow : s[e]);
+  }
+  if constexpr (KIND == GEMM_W8A8 && ACC_OUT) *reinterpret_cast<i32x4_t*>(acc_out + (int64_t)m * ld_acc + n) = s;
+  if constexpr (OUT_BF16) {
+    uint16_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, (__bf16)y[e]);
+    const uint2 w = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(C) + (int64_t)m * ldc + n) = w;
+  } else {
+    *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(C) + (int64_t)m * ldc + n) = f32x4_t{y[0], y[1], y[2], y[3]};
+  }
+}
+
 // Launch plan of the small-M path for one product shape (splits == 1: no
 // partial sums in the workspace).
 struct SkPlan {
@@ -663,10 +714,19 @@ static hipError_t launch_skinny_fm(const GemmArgs& g, const SkPlan& p, hipStream
 
 template <int KIND>
 static hipError_t launch_reduce(const GemmArgs& g, int splits, hipStream_t stream) {
-  const dim3 rgrid((unsigned)((g.n + 255) / 256), (unsigned)g.m), rblock(256);
+  const auto al = [](const void* q, uintptr_t b) { return ((uintptr_t)q & (b - 1)) == 0; };
+  const bool four = g.n % 4 == 0 && g.ldc % 4 == 0 && al(g.c, g.c_bf16 ? 8 : 16) && al(g.part, 16) &&
+                    (!g.acc_out || (g.ld_acc % 4 == 0 && al(g.acc_out, 16)));
+  const dim3 rgrid((unsigned)((four ? g.n / 4 + 255 : g.n + 255) / 256), (unsigned)g.m), rblock(256);
 #define TP_LAUNCH_RED(OB, AO)                                                                                     \
-  hipLaunchKernelGGL((k_qgemm_reduce<KIND, OB, AO>), rgrid, rblock, 0, stream, g.part, splits, (int)g.m,          \
-                     (int)g.n, g.w_scales, g.a_scales, g.c, g.ldc, g.acc_out, g.ld_acc)
+  do {                                                                                                            \
+    if (four)                                                                                                     \
+      hipLaunchKernelGGL((k_qgemm_reduce4<KIND, OB, AO>), rgrid, rblock, 0, stream, g.part, splits, (int)g.m,     \
+                         (int)g.n, g.w_scales, g.a_scales, g.c, g.ldc, g.acc_out, g.ld_acc);                     \
+    else                                                                                                          \
+      hipLaunchKernelGGL((k_qgemm_reduce<KIND, OB, AO>), rgrid, rblock, 0, stream, g.part, splits, (int)g.m,      \
+                         (int)g.n, g.w_scales, g.a_scales, g.c, g.ldc, g.acc_out, g.ld_acc);                     \
+  } while (0)
   if (KIND == GEMM_W8A8 && g.acc_out) {
     if (g.c_bf16) TP_LAUNCH_RED(true, true); else TP_LAUNCH_RED(false, true);
   } else {
