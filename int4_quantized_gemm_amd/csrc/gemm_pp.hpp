@@ -250,10 +250,13 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
   // the group being summed (cu, per column): the raw products of group g are
   // added as they come, and on entering group g+1 the accumulator is
   // multiplied by s[g]/s[g+1]. A group whose scale is zero, or more than 2^64
-  // times smaller than the running unit (where the rescale could overflow),
-  // has its codes masked off; a column with a skipped nonzero scale is
-  // recomputed exactly in the epilogue (fix bit).
+  // times smaller than the largest scale taken so far in the column (cmx:
+  // every earlier group's sum is then held at most 2^64 times its own size,
+  // so the running sum cannot overflow through the rescales however the
+  // scales step down), has its codes masked off; a column with a skipped
+  // nonzero scale is recomputed exactly in the epilogue (fix bit).
   float cu[KIND == GEMM_W4 ? FN : 1];
+  float cmx[KIND == GEMM_W4 ? FN : 1];
   uint32_t mk[KIND == GEMM_W4 ? FN : 1];
   int fix = 0;
   // W4A8: the fp32 sum of the folded groups (the int32 acc holds one group).
@@ -303,11 +306,12 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const float s = s_nx[j];
-      const bool use = (s != 0.f) && (cu[j] <= s * 0x1p64f);  // false for NaN
+      const bool use = (s != 0.f) && (cmx[j] <= s * 0x1p64f);  // false for NaN
       const float r = use ? cu[j] / s : 1.f;
 #pragma unroll
       for (int i = 0; i < FM; ++i) acc[i][j] *= r;
       cu[j] = use ? s : cu[j];
+      cmx[j] = use ? fmaxf(cmx[j], s) : cmx[j];
       mk[j] = use ? 0xF0F0F0F0u : 0u;
       fix |= (!use && s != 0.f) ? (1 << j) : 0;
     }
@@ -500,6 +504,7 @@ __global__ __launch_bounds__(512, 1) void k_qgemm_pp(
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       cu[j] = 0.f;
+      cmx[j] = 0.f;
       s_nx[j] = sw[(int64_t)min(n0 + wn0 + j * 16 + r16, N - 1) * groups + (ks0 >> 2)];
     }
   }

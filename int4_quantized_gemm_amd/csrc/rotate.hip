@@ -348,8 +348,8 @@ struct DequantSrc {
 // The SwiGLU feed-forward's hidden activation h = bf16(silu(g) * u), silu(x)
 // = x / (1 + e^-x), rounded once (to nearest even) from its fp64 evaluation
 // (tensai docs, "画像生成", section "何が走るか": every block is attention plus
-// a SwiGLU feed-forward; TensorFold pull request #948: bf16 activations
-// rounded where the reference rounds them).
+// a SwiGLU feed-forward; TensorFold pull request #948, first comment: the
+// activations between operations are kept in bf16).
 //
 // fp32 first: e = v_exp_f32(-g * fl(log2 e)), h = (g u) v_rcp_f32(1 + e).
 // Relative error, to first order, with u = 2^-24: the exponent argument is

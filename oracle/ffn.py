@@ -7,8 +7,8 @@ Sources:
   every transformer block is attention followed by a SwiGLU feed-forward.
 * same page, section "幅とメモリ" (width and memory): the input of each
   product is rotated per 256 columns on the device before it is used.
-* TensorFold pull request #948: activations are bf16, rounded where the
-  reference rounds them.
+* TensorFold pull request #948, first comment: the activations between
+  operations are kept in bf16.
 
 Readings (also in the design notes):
   R15 SwiGLU(g, u) = silu(g) * u with silu(x) = x / (1 + e^-x) (the pages name

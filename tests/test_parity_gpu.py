@@ -63,7 +63,7 @@ def test_rotate_quantize_int8_full(name):
     _check_weights(w, 8, d)
 
 
-@pytest.mark.parametrize("name", ["tiny", "proj256", "ffn_down"])
+@pytest.mark.parametrize("name", ["tiny", "proj256", "ffn_down", "dit_qkv", "dit_out", "dit_gateup", "dit_down"])
 def test_rotate_quantize_int4_full(name):
     d = dev()
     wl = W.BY_NAME[name]
@@ -130,6 +130,27 @@ def test_rotate_rows(xd, yd, m, k):
         # of the two ends of the fp32 error interval
         assert np.all((lo <= got) & (got <= hi)), "bf16 rotation is not a rounding of a value within the bound"
         assert np.mean(got != oracle.bf16_round(exact)) < 1e-2
+
+
+@pytest.mark.parametrize("name", ["ffn_up", "ffn_down"])
+def test_rotate_rows_full_size(name):
+    """The launches the benchmark times (full 4096x3072 and 4032x12288 bf16
+    activations to bf16), each output checked directly against the exact
+    rotation on sampled whole rows: a correct bf16 rounding of a value within
+    the fp32 transform's error bound."""
+    d = dev()
+    wl = W.BY_NAME[name]
+    announce("tp_hadamard_rotate_rows full size", name, wl.m, wl.k)
+    x = W.generate_activations(wl)
+    y = tp.tp_hadamard_rotate_rows(x.to(d), out_dtype=torch.bfloat16)
+    sel = sample_rows(wl.m, 200, seed=wl.seed)
+    x64 = f64(x)[sel]
+    exact = oracle.rotate_groups(x64)
+    bound = rotation_error_bound(x64)
+    got = f64(y)[sel]
+    lo, hi = oracle.bf16_round(exact - bound), oracle.bf16_round(exact + bound)
+    assert np.all((lo <= got) & (got <= hi)), "bf16 rotation is not a rounding of a value within the bound"
+    assert np.mean(got != oracle.bf16_round(exact)) < 1e-2
 
 
 def test_rotate_rows_in_place_and_subview():
@@ -294,15 +315,19 @@ def test_w4_group_scale_edges(m, n, k):
     """Hand-made int4 codes and group scales that the quantizer never emits,
     one pattern per column class, on the split-K, 128x192 and 256x192 paths:
     zero scales over nonzero codes (no contribution), scales 1e28 apart in
-    both orders, all-zero scales, and columns whose only nonzero codes sit in
-    the tiny-scale groups. Each class is compared on its own columns."""
+    both orders, all-zero scales, columns whose only nonzero codes sit in
+    the tiny-scale groups, and a staircase of scales each 2^60 below the one
+    before (1, 2^-60, 2^-120, repeated): every step is within 2^64 of the
+    previous scale, but the third is 2^120 below the first, so a rescale
+    bounded by the previous step alone would overflow the running sum. Each
+    class is compared on its own columns."""
     d = dev()
     announce("tp_qgemm_w4 group-scale edges", m, n, k)
     rng = np.random.default_rng(m + n + k)
     g = k // 256
     codes = rng.integers(-7, 8, size=(n, k)).astype(np.int8)
     s = (rng.uniform(0.5, 2.0, size=(n, g)) * 1e-2).astype(np.float32)
-    cls = np.arange(n) % 6
+    cls = np.arange(n) % 7
     tiny = np.float32(1e-30)
     s[cls == 1, 0] = 0.0                                   # zero scale over nonzero codes
     s[cls == 2, 1::2] = tiny                               # normal, tiny, normal, ...
@@ -312,6 +337,8 @@ def test_w4_group_scale_edges(m, n, k):
     c5 = codes[cls == 5].reshape(-1, g, 256)
     c5[:, 0::2] = 0
     codes[cls == 5] = c5.reshape(-1, k)
+    stair = np.ldexp(np.float32(1.0), -60 * (np.arange(g) % 3)).astype(np.float32)
+    s[cls == 6] = stair                                    # 1, 2^-60, 2^-120, 1, ...
     packed = oracle.pack_int4(codes)
     x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
     y = tp.tp_qgemm_w4(x.to(d), torch.from_numpy(packed).to(d), torch.from_numpy(s).to(d), rotate=False,
@@ -320,7 +347,7 @@ def test_w4_group_scale_edges(m, n, k):
     ref = oracle.qgemm_w4(f64(x), packed, s, rotate=False)
     assert np.all(np.isfinite(got))
     assert np.all(got[:, cls == 4] == 0.0)
-    for c in (0, 1, 2, 3, 5):
+    for c in (0, 1, 2, 3, 5, 6):
         err = np.linalg.norm(got[:, cls == c] - ref[:, cls == c]) / np.linalg.norm(ref[:, cls == c])
         assert err < 1e-5, f"column class {c}: relative error {err:.3e}"
 
