@@ -58,6 +58,7 @@ def parse():
     p.add_argument("--only", default=None,
                    help="run only the launches whose name contains this text (for counter profiling)")
     p.add_argument("--no-next", action="store_true", help="skip the rows measured beside the step (\"next\")")
+    p.add_argument("--no-small-m", action="store_true", help="skip the M <= 64 rows of the default run")
     p.add_argument("--next-only", action="store_true",
                    help="measure only the rows beside the step and print their JSON (for profiling)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -104,59 +105,117 @@ def _traffic_for(kernel_key):
 
 
 # --------------------------------------------------------------- CPU baseline
-def cpu_baseline(rows):
-    """The oracle as it stands, on the first `rows` activation rows of every
-    product of the step (weights quantized by the oracle first, untimed)."""
+def _cpu_model():
+    """The host CPU's model name (the first "model name" of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_inputs(rows):
+    """Activations (the first `rows` rows; 0: all) and the oracle's own
+    quantized weights for every product of the step (untimed)."""
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    total_ops = 0.0
-    total_s = 0.0
-    parts = []
+    out = []
     for kind, wl in step_plan():
         x, w = W.generate(wl, rows=rows or None)
-        x64 = x.double().numpy()
         wn = w.numpy()
         if kind == "w4":
             q, s = oracle.quantize_weights_int4(wn)
-            fn = lambda: oracle.qgemm_w4(x64, q, s)
+            wd = oracle.dequantize_int4(q, s)
         else:
             q, s = oracle.quantize_weights_int8(wn)
-            fn = (lambda: oracle.qgemm_w8(x64, q, s)) if kind == "w8" else (lambda: oracle.qgemm_w8a8(x64, q, s))
-        del w, wn
-        times = []
-        for _ in range(3):
+            wd = oracle.dequantize_int8(q, s) if kind == "w8" else None
+        out.append((kind, wl, x.double().numpy(), q, s, wd))
+    return out
+
+
+def _oracle_pass(inputs, rows, repeats):
+    """The oracle as it stands over the first `rows` activation rows of every
+    product of the step, each step of the path timed on its own: activation
+    rotation (the dense H product per 256-group), activation quantization
+    (W8A8) or the bf16 rounding of the rotated operand (W8, W4), the product
+    (fp64 matrix product: exact on the integer codes of W8A8, against the
+    dequantized weights for W8 and W4) and the W8A8 scale epilogue. Returns
+    (ops, {step: seconds, each the median over repeats}, {product: seconds})."""
+    import oracle
+    steps = {"rotation": 0.0, "quantization": 0.0, "product": 0.0, "epilogue": 0.0}
+    per = {}
+    total_ops = 0.0
+    for kind, wl, xall, q, s, wd in inputs:
+        x64 = xall[:rows] if rows else xall
+        times = {k: [] for k in steps}
+        for _ in range(repeats):
             t0 = time.perf_counter()
-            fn()
-            times.append(time.perf_counter() - t0)
-        dt = float(np.median(times))
-        ops = 2.0 * x.shape[0] * wl.n * wl.k
-        total_ops += ops
-        total_s += dt
-        parts.append(f"{wl.name}:{dt:.2f}s")
+            xr = oracle.rotate_groups(x64)
+            t1 = time.perf_counter()
+            if kind == "w8a8":
+                qa, sa = oracle.quantize_activations_int8(xr, rotate=False)
+                t2 = time.perf_counter()
+                acc = oracle.int_accumulate(qa, q)
+                t3 = time.perf_counter()
+                _ = acc.astype(np.float64) * sa.astype(np.float64)[:, None] * s.astype(np.float64)[None, :]
+                t4 = time.perf_counter()
+            else:
+                xb = oracle.bf16_round(xr)
+                t2 = time.perf_counter()
+                _ = np.matmul(xb, wd.T)
+                t3 = t4 = time.perf_counter()
+            for k, dt in zip(steps, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
+                times[k].append(dt)
+        med = {k: float(np.median(v)) for k, v in times.items()}
+        for k in steps:
+            steps[k] += med[k]
+        per[wl.name] = sum(med.values())
+        total_ops += 2.0 * x64.shape[0] * wl.n * wl.k
+    return total_ops, steps, per
+
+
+def cpu_baseline(rows):
+    """The oracle timed on the host: all threads on `rows` rows of every
+    product (0: all rows), then one thread on a 64-row sample."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    inputs = _oracle_inputs(rows)
+    ops, steps, per = _oracle_pass(inputs, 0, repeats=5)
+    total = sum(steps.values())
+    one_rows = 64
+    with threadpool_limits(limits=1):
+        ops1, steps1, _ = _oracle_pass(inputs, one_rows, repeats=3)
+    total1 = sum(steps1.values())
     return {
-        "value": total_ops / total_s / 1e12,
+        "value": ops / total / 1e12,
         "unit": "TOPS",
         "cores": int(cores),
         "kind": "oracle",
+        "cpu_model": _cpu_model(),
+        "host_cpus": os.cpu_count(),
         "sample": f"{'first %d' % rows if rows else 'all'} activation rows of each of the 6 products of the step "
-                  f"(all N, all K), "
-                  f"fp64 numpy oracle incl. rotation, quantization, dequantization and product; median of 3 runs, "
-                  f"{total_s:.1f} s per pass ({', '.join(parts)})",
+                  f"(all N, all K), fp64 numpy oracle: rotation, quantization or bf16 rounding, product, epilogue; "
+                  f"median of 5 runs per step, {total:.1f} s per pass "
+                  f"({', '.join(f'{k}:{v:.2f}s' for k, v in per.items())})",
+        "steps_s": {k: round(v, 4) for k, v in steps.items()},
+        "one_thread": {"value": ops1 / total1 / 1e12, "unit": "TOPS", "cores": 1,
+                       "sample": f"first {one_rows} activation rows of each product, median of 3 runs per step, "
+                                 f"{total1:.1f} s per pass",
+                       "steps_s": {k: round(v, 4) for k, v in steps1.items()}},
     }
 
 
 # ------------------------------------------------------- M <= 64 sweep (HBM)
-def small_m_sweep(args):
+def small_m_sweep(args, emit=False):
     """Products with 1, 16 and 64 activation rows against the full-size
     weights of the step. They are bound by reading the weights, so each case
     cycles through enough distinct copies of the packed weight (at least
     2 x 256 MB) that no launch finds its weight in the 256 MB last-level cache.
-    Bytes per launch = weight codes + scales + activation operand + output."""
+    Bytes per launch = weight codes + scales + activation operand + output.
+    Returns one dict per case (and prints each as a JSON line if emit)."""
     import torch
     import int4_quantized_gemm_amd as tp
     import workloads as W
@@ -164,6 +223,7 @@ def small_m_sweep(args):
     d = torch.device("cuda:0")
     torch.cuda.set_device(d)
     cases = [("w8", W.FFN_UP), ("w4", W.FFN_DOWN), ("w8a8", W.DIT_QKV), ("w8a8", W.DIT_GATEUP)]
+    out_rows = []
     for kind, wl in cases:
         _, w = W.generate(wl, rows=1)
         bits = 4 if kind == "w4" else 8
@@ -215,13 +275,16 @@ def small_m_sweep(args):
             del graph
             t_med, t_min = float(np.median(med)), float(np.min(med))
             gbs = nbytes / t_med / 1e9
-            print(json.dumps({"metric": "small-M product HBM bandwidth", "case": f"{kind}[{wl.name}]", "m": m,
-                              "n": wl.n, "k": wl.k, "bytes": nbytes, "us_median": round(t_med * 1e6, 2),
-                              "us_min": round(t_min * 1e6, 2), "gbs": round(gbs, 1),
-                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "weight_copies": copies,
-                              "tflops": round(2.0 * m * wl.n * wl.k / t_med / 1e12, 2)}), flush=True)
+            row = {"case": f"{kind}[{wl.name}]", "m": m, "n": wl.n, "k": wl.k, "bytes": nbytes,
+                   "us_median": round(t_med * 1e6, 2), "us_min": round(t_min * 1e6, 2), "gbs": round(gbs, 1),
+                   "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "weight_copies": copies,
+                   "tflops": round(2.0 * m * wl.n * wl.k / t_med / 1e12, 2)}
+            out_rows.append(row)
+            if emit:
+                print(json.dumps({"metric": "small-M product HBM bandwidth", **row}), flush=True)
         del qs
         torch.cuda.empty_cache()
+    return out_rows
 
 
 # ------------------------------------------ rows measured beside the step
@@ -480,7 +543,7 @@ def main():
         print(json.dumps(cpu_baseline(args.cpu_rows)))
         return
     if args.small_m:
-        small_m_sweep(args)
+        small_m_sweep(args, emit=True)
         return
     if args.library_reference:
         library_reference(args)
@@ -585,30 +648,80 @@ def main():
     torch.cuda.synchronize()
     per = []
     for i, (name, kind, units, _) in enumerate(launches):
-        ms = float(np.mean([evb[s][i][0].elapsed_time(evb[s][i][1]) for s in range(args.steps)]))
+        ts = [evb[s][i][0].elapsed_time(evb[s][i][1]) for s in range(args.steps)]
+        ms = float(np.median(ts))
         ach, peak, unit = rate(kind, units, ms)
-        per.append({"launch": name, "us": round(ms * 1e3, 2), "achieved": round(ach, 1), "unit": unit,
-                    "peak": peak, "frac": round(ach / peak, 4), "bound": "hbm" if kind == "hbm" else "mfma",
-                    "units": units})
+        per.append({"launch": name, "us": round(ms * 1e3, 2), "us_min": round(float(np.min(ts)) * 1e3, 2),
+                    "achieved": round(ach, 1), "unit": unit, "peak": peak, "frac": round(ach / peak, 4),
+                    "bound": "hbm" if kind == "hbm" else "mfma", "units": units, "kind": kind})
     dom_i = max(range(len(per)), key=lambda i: per[i]["us"])
 
-    # Timed region: K steps, events only around the dominant launch (its
-    # roofline figure comes from these).
+    # Timed region: K steps, an event pair around each step and one around
+    # the dominant launch (its roofline figure comes from these).
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in launches]
           for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_i in range(args.steps):
+        evs[s_i][0].record()
         run_step(ev[s_i], only=dom_i)
+        evs[s_i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dom_ms = float(np.mean([ev[s][dom_i][0].elapsed_time(ev[s][dom_i][1]) for s in range(args.steps)]))
+    dom_ts = [ev[s][dom_i][0].elapsed_time(ev[s][dom_i][1]) for s in range(args.steps)]
+    dom_ms = float(np.median(dom_ts))
+    step_ts = [evs[s][0].elapsed_time(evs[s][1]) for s in range(args.steps)]
     name, kind, units, _ = launches[dom_i]
     ach, peak, unit = rate(kind, units, dom_ms)
-    dom = {"launch": name, "us": round(dom_ms * 1e3, 2), "achieved": round(ach, 1), "unit": unit, "peak": peak,
-           "frac": round(ach / peak, 4), "bound": "hbm" if kind == "hbm" else "mfma"}
     ms_per_step = wall / args.steps * 1e3
     value = step_ops / (wall / args.steps) / 1e12
+
+    # The shader clock the GPU runs this step at: amd-smi polled while the
+    # step repeats for about a second, outside the timed region.
+    clock = sample_clock(run_step, torch, seconds=1.5)
+    clk = clock.get("sclk_mhz_median")
+    dom = {"launch": name, "us": round(dom_ms * 1e3, 2), "us_min": round(float(np.min(dom_ts)) * 1e3, 2),
+           "achieved": round(ach, 1), "unit": unit, "peak": peak, "frac": round(ach / peak, 4),
+           "bound": "hbm" if kind == "hbm" else "mfma"}
+
+    # The int8 path at M = 4096, K = 3072 (qkv, out, gate+up): quantizer and
+    # product per projection, and together.
+    k3072 = {}
+    tot_us = tot_q_us = tot_ops = 0.0
+    for e in plan:
+        wl = e["wl"]
+        if e["kind"] != "w8a8" or wl.k != 3072:
+            continue
+        qn, gn = f"rotate_quantize_i8[{wl.name}]", f"gemm_w8a8[{wl.name}]"
+        byname = {r["launch"]: r for r in per}
+        if qn not in byname or gn not in byname:  # --only
+            continue
+        qr, gr = byname[qn], byname[gn]
+        ops = 2.0 * wl.m * wl.n * wl.k
+        k3072[wl.name] = {"n": wl.n, "gemm_us": gr["us"], "gemm_tops": round(ops / gr["us"] / 1e6, 1),
+                          "gemm_frac": round(ops / gr["us"] / 1e6 / PEAK_TOPS_I8, 4), "quantize_us": qr["us"],
+                          "with_quantize_tops": round(ops / (gr["us"] + qr["us"]) / 1e6, 1)}
+        tot_us += gr["us"]
+        tot_q_us += qr["us"]
+        tot_ops += ops
+    k3072_summary = None if not k3072 else {"projections": k3072, "gemm_tops": round(tot_ops / tot_us / 1e6, 1),
+                     "gemm_frac": round(tot_ops / tot_us / 1e6 / PEAK_TOPS_I8, 4),
+                     "with_quantize_tops": round(tot_ops / (tot_us + tot_q_us) / 1e6, 1),
+                     "with_quantize_frac": round(tot_ops / (tot_us + tot_q_us) / 1e6 / PEAK_TOPS_I8, 4),
+                     "note": "M=4096, K=3072 W8A8 projections of the block (qkv, out, gate+up): the i8 products "
+                             "alone and with their activation rotation + quantization; medians of the breakdown "
+                             "pass"}
+    # The step against its own roofline: every launch at its peak (i8 or
+    # bf16 MFMA, or HBM) against the measured step.
+    ideal_us = 0.0
+    for r in per:
+        if r["kind"] == "hbm":
+            ideal_us += r["units"] / (PEAK_HBM_GBS * 1e3)
+        elif r["kind"] == "i8":
+            ideal_us += r["units"] / (PEAK_TOPS_I8 * 1e6)
+        else:
+            ideal_us += r["units"] / (PEAK_TFLOPS_BF16 * 1e6)
 
     result = {
         "metric": METRIC,
@@ -639,20 +752,86 @@ def main():
             "frac": dom["frac"],
             "traffic": _traffic_for(dom["launch"]),
             "us": dom["us"],
+            "us_min": dom["us_min"],
+            "frac_at_measured_clock": round(dom["frac"] * 2400.0 / clk, 4) if clk else None,
         },
-        "breakdown": [{k: r[k] for k in ("launch", "us", "achieved", "unit", "frac")} for r in per],
+        "step_ms": {"median": round(float(np.median(step_ts)), 4), "min": round(float(np.min(step_ts)), 4),
+                    "median_over_min": round(float(np.median(step_ts) / np.min(step_ts)), 4),
+                    "note": "HIP events around each step of the timed region"},
+        "step_roofline": {"ideal_us": round(ideal_us, 1), "measured_us": round(ms_per_step * 1e3, 1),
+                          "frac": round(ideal_us / (ms_per_step * 1e3), 4),
+                          "note": "every launch of the step at its own peak (i8 MFMA 5.0 POP/s, bf16 MFMA "
+                                  "2.5 PFLOP/s, HBM 8 TB/s) against the measured step"},
+        "k3072_int8_path": k3072_summary,
+        "clock": clock,
+        "breakdown": [{k: r[k] for k in ("launch", "us", "us_min", "achieved", "unit", "frac")} for r in per],
         "breakdown_note": "per-launch HIP events in a pass of their own before the timed region (events around "
-                          "every launch cost about 90 us per step); the timed region has events around the "
-                          "dominant launch only",
+                          "every launch cost about 90 us per step); median and min over the steps; the timed "
+                          "region has events around each step and around the dominant launch only",
         "weight_prep": {"gbs_fp32_read": round(prep_bytes / prep_s / 1e9, 1), "seconds": round(prep_s, 4),
                         "note": "tp_rotate_quantize_weights over every weight of the step, once, untimed in value"},
         "cpu_baseline": None,
     }
+    if not args.only and not args.no_small_m:
+        rows = small_m_sweep(args)
+        by_m = {}
+        for r in rows:
+            by_m.setdefault(r["m"], []).append(r["frac_hbm"])
+        result["small_m"] = {"rows": rows, "min_frac_hbm_by_m": {str(m): min(v) for m, v in by_m.items()},
+                             "note": "M <= 64 products against the full-size step weights, cycled through >= 512 "
+                                     "MB of weight copies (no last-level-cache hits); bytes = weight codes + "
+                                     "scales + activations + output; median of 5 graph replays"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows)
     if not args.no_next and not args.only:
         result["next"] = next_rows(args, cpu=not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
+
+
+def sample_clock(run_step, torch, seconds=1.5):
+    """Median shader clock (MHz, over samples and XCDs) reported by amd-smi
+    while the step repeats; {} where amd-smi is not usable."""
+    import shutil
+    import subprocess
+    import threading
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        # under the profiler every launch is serialized (the clock means
+        # nothing) and a child program would inherit the profiler's library
+        return {"sclk_mhz_median": None, "samples": 0, "source": "not sampled under a profiler"}
+    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    samples = []
+    stop = threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([smi, "metric", "-c", "--json"], capture_output=True, text=True, timeout=5)
+                j = json.loads(r.stdout[r.stdout.index("{"):] if "{" in r.stdout else r.stdout)
+                gd = j["gpu_data"][0] if isinstance(j, dict) else j[0]
+                clks = [v["clk"]["value"] for k, v in gd["clock"].items()
+                        if k.startswith("gfx") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
+                        and isinstance(v["clk"].get("value"), (int, float))]
+                if clks:
+                    samples.append(float(np.mean(clks)))
+            except Exception:
+                return
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        run_step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=10)
+    if not samples:
+        return {"sclk_mhz_median": None, "samples": 0, "source": "amd-smi metric -c (not available)"}
+    return {"sclk_mhz_median": round(float(np.median(samples)), 1), "sclk_mhz_min": round(float(np.min(samples)), 1),
+            "sclk_mhz_max": round(float(np.max(samples)), 1), "samples": len(samples),
+            "source": "amd-smi metric -c, mean over XCDs, polled while the step repeats for about 1.5 s "
+                      "(outside the timed region)",
+            "note": "peak figures are the published 2.4 GHz ones; frac_at_measured_clock rescales the dominant "
+                    "launch's fraction to this clock"}
 
 
 if __name__ == "__main__":
