@@ -303,6 +303,9 @@ struct Raw16<float> {
 template <typename T>
 struct RowSrc {
   typedef T raw_elem;
+  // The fast int8 kernel may load a group's inputs again for its exact
+  // fallbacks instead of keeping them in registers.
+  static constexpr bool REREAD = true;
   const T* x;
   int64_t ldx;
   __device__ __forceinline__ void load8(int64_t r, int64_t c, float (&v)[8]) const { tp::load8(x + r * ldx + c, v); }
@@ -323,6 +326,7 @@ struct RowSrc {
 template <int BITS>
 struct DequantSrc {
   typedef float raw_elem;
+  static constexpr bool REREAD = false;
   const uint8_t* q;
   int64_t ldq;  // bytes
   const float* s;
@@ -389,6 +393,7 @@ __device__ __noinline__ uint32_t swiglu_exact(float g, float u) {
 template <typename T>
 struct SwigluSrc {
   typedef uint16_t raw_elem;
+  static constexpr bool REREAD = false;  // h is computed, not loaded: keep it
   const T* g;
   int64_t ldg;
   const T* u;
@@ -491,12 +496,18 @@ template <typename TIn>
 __device__ __forceinline__ double exact_elem(const Raw16<TIn>& raw, bool rotate, int e, int l16) {
   double acc = 0.0;
   if (rotate) {
-    const int lpar = __builtin_popcount((unsigned)(l16 & (e >> 4))) & 1;
+    // Bit i of w: the parity of popcount((16 l16 + i) & e), i.e. the sign of
+    // input i of this lane. The parity is linear in e, so the low half is the
+    // xor of the Walsh rows of e's low bits (0xAAAA for bit 0, 0xCCCC, 0xF0F0,
+    // 0xFF00) and the lane's part flips all sixteen.
+    const int el = e & 15;
+    uint32_t w = ((el & 1) ? 0xAAAAu : 0u) ^ ((el & 2) ? 0xCCCCu : 0u) ^ ((el & 4) ? 0xF0F0u : 0u) ^
+                 ((el & 8) ? 0xFF00u : 0u);
+    if (__builtin_popcount((unsigned)(l16 & (e >> 4))) & 1) w ^= 0xFFFFu;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int par = lpar ^ (__builtin_popcount((unsigned)(i & e)) & 1);
-      const double xi = (double)raw.get(i);
-      acc += par ? -xi : xi;
+      const uint64_t xb = __builtin_bit_cast(uint64_t, (double)raw.get(i));
+      acc += __builtin_bit_cast(double, xb ^ ((uint64_t)((w >> i) & 1u) << 63));
     }
   } else {
     // input e lives in lane e / 16, register e % 16
@@ -517,13 +528,16 @@ constexpr float RQ_MAGIC = 12582912.0f;  // 1.5 * 2^23: adding it rounds to an i
 
 // WPR = 1: one wave per row, four rows per block (k <= 12 * 256).
 // WPR = 4: one block per row, the four waves split the groups (k <= 48 * 256).
-// Three waves per SIMD: the register budget (166) that keeps every input in
-// registers for the exact fallbacks without spilling.
-template <typename Src, int WPR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_rotq_i8_fast(Src src, int64_t rows,
-                                                      int groups, int rotate, int8_t* __restrict__ q, int64_t ldq,
-                                                      float* __restrict__ scales) {
+// Sources that are plain rows (REREAD) load a group's inputs again for the
+// rare exact fallbacks, which fits the kernel in 128 registers: four waves per
+// SIMD, so the 4096 one-wave rows of a 4096 x 3072 input are all resident at
+// once. Computed sources (SwiGLU) keep their inputs in registers for the
+// fallbacks, within the 168 registers of three waves per SIMD.
+template <typename Src, int WPR, int WPE = Src::REREAD ? 4 : 3>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k_rotq_i8_fast(
+    Src src, int64_t rows, int groups, int rotate, int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales) {
   typedef typename Src::raw_elem TIn;
+  constexpr bool KEEP = !Src::REREAD;
   constexpr int NU = 3;  // groups per 16-lane set
   constexpr int NWB = 4;  // waves per block
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -548,7 +562,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
 
   // Load every group of this wave (up to 3 per 16-lane row) and transform it.
-  Raw16<TIn> raw[NU];
+  Raw16<TIn> raw[KEEP ? NU : 1];  // the inputs, kept for the exact fallbacks
   float v[NU][16];
   float bnd[NU];
   bool has[NU];
@@ -561,17 +575,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
+      Raw16<TIn> r0;
       if (has[u])
-        src.finish(row, (int64_t)(gb + set + 4 * u) * 256 + l16 * 16, st[u], raw[u]);
+        src.finish(row, (int64_t)(gb + set + 4 * u) * 256 + l16 * 16, st[u], r0);
       else
-        raw[u].zero();
+        r0.zero();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[u][i] = r0.get(i);
+      if constexpr (KEEP) raw[u] = r0;
     }
   }
+  // The inputs of unit U for an exact fallback (every lane of the row takes
+  // part; lanes without the group read zeros).
+  auto inputs = [&](auto uc) -> Raw16<TIn> {
+    constexpr int U = decltype(uc)::value;
+    if constexpr (KEEP) {
+      return raw[U];
+    } else {
+      Raw16<TIn> r;
+      if (has[U])
+        src.load16(row, (int64_t)(gb + set + 4 * U) * 256 + l16 * 16, r);
+      else
+        r.zero();
+      return r;
+    }
+  };
   float amax = 0.f, bmax = 0.f;
+  float umax[NU];  // this lane's largest |value| of each unit
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[u][i] = raw[u].get(i);
     bnd[u] = 0.f;
     if (rotate) {
       float l1 = 0.f;
@@ -585,8 +617,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     } else {
       transpose16(v[u], fbuf, l16);
     }
+    umax[u] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
+    for (int i = 0; i < 16; ++i) umax[u] = fmaxf(umax[u], fabsf(v[u][i]));
+    amax = fmaxf(amax, umax[u]);
     bmax = fmaxf(bmax, bnd[u]);
   }
   amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
@@ -621,10 +655,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     double m_ex = 0.0;
     auto scan = [&](auto uc) {
       constexpr int U = decltype(uc)::value;
+      // units with no lane reaching the threshold hold no candidate
+      if (!__ballot(has[U] && umax[U] >= thr)) return;
       uint32_t bits = 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) bits |= (uint32_t)(has[U] && fabsf(v[U][r]) >= thr) << r;
       uint32_t rmask = or16(bits);  // registers that hold a candidate in some lane of this row
+      if (!__ballot(rmask != 0u)) return;
+      const Raw16<TIn> xin = inputs(uc);
       while (rmask) {               // uniform over this 16-lane row
         const int r = __builtin_ctz(rmask);
         rmask &= rmask - 1;
@@ -632,7 +670,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         while (lmask) {
           const int lc = __builtin_ctz(lmask);
           lmask &= lmask - 1;
-          m_ex = fmax(m_ex, fabs(exact_elem(raw[U], true, lc + 16 * r, l16)));
+          m_ex = fmax(m_ex, fabs(exact_elem(xin, true, lc + 16 * r, l16)));
         }
       }
     };
@@ -655,25 +693,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const double inv64 = s > 0.0f ? 1.0 / s64 : 0.0;
   const float inv = (float)(inv64 * unscale);  // applied to the unnormalized outputs
 
-  // Codes, one group at a time. t = v * inv clamped to [-127, 127] (clamping
-  // first only removes cases that clamp either way); t + 1.5 * 2^23 rounds to
-  // the nearest integer, whose two's complement sits in the low byte. Codes
-  // the fp32 bound cannot decide get the exact value and the reference rule.
+  // Codes, one group at a time. f = v * inv + 1.5 * 2^23 in one fused
+  // rounding holds the nearest integer to the exact product v * inv in its
+  // low bits (two's complement in the low byte), and d = v * inv - (f - 1.5 *
+  // 2^23), again fused, its distance from that integer. A code is decided when
+  // |d| < lim: the fp32 transform (within bnd of the exact value, times inv),
+  // the rounding of inv and of d stay below 0.5 - lim, so the exact quotient
+  // rounds to the same integer, which is then within [-127, 127] (|exact| <=
+  // 127.5 - ...). A lane flag collects undecided codes; only a wave holding one
+  // rebuilds the per-element bits and takes the exact path (the reference
+  // rule on the exact value). A scale so small that inv overflows to
+  // infinity makes d NaN: such codes are undecided too.
   int8_t* qr = q + row * ldq;
   auto codes = [&](auto uc) {
     constexpr int U = decltype(uc)::value;
     uint32_t code[16];
-    uint32_t bits = 0;
     const float lim = 0.5f - (bnd[U] * inv * 1.0001f + 129.f * 0x1p-22f);
+    bool undecided = false;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float t = __builtin_amdgcn_fmed3f(v[U][r] * inv, -127.f, 127.f);
-      const float f = t + RQ_MAGIC;
-      bits |= (uint32_t)(has[U] && fabsf(t - (f - RQ_MAGIC)) >= lim) << r;
+      const float f = fmaf(v[U][r], inv, RQ_MAGIC);
+      const float d = fmaf(v[U][r], inv, RQ_MAGIC - f);
+      undecided |= !(fabsf(d) < lim);  // NaN (inv overflowed for a tiny scale): undecided
       code[r] = __builtin_bit_cast(uint32_t, f);
     }
-    if (__ballot(bits != 0u)) {
+    if (__ballot(undecided && has[U])) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float f = fmaf(v[U][r], inv, RQ_MAGIC);
+        const float d = fmaf(v[U][r], inv, RQ_MAGIC - f);
+        bits |= (uint32_t)(has[U] && !(fabsf(d) < lim)) << r;
+      }
       uint32_t rmask = or16(bits);
+      const Raw16<TIn> xin = inputs(uc);
       while (rmask) {  // uniform over this 16-lane row
         const int r = __builtin_ctz(rmask);
         rmask &= rmask - 1;
@@ -681,7 +734,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         while (lmask) {
           const int lc = __builtin_ctz(lmask);
           lmask &= lmask - 1;
-          const double xe = exact_elem(raw[U], rotate != 0, lc + 16 * r, l16);
+          const double xe = exact_elem(xin, rotate != 0, lc + 16 * r, l16);
           const uint32_t c = (uint32_t)quant_code(xe * unscale, s64, inv64, 127.0);
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) code[rr] = (rr == r && l16 == lc) ? c : code[rr];
