@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TP_ABI_VERSION 7
+#define TP_ABI_VERSION 8
 
 typedef enum tp_status {
   TP_OK = 0,
@@ -357,6 +357,30 @@ tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float
                                      void* c, tp_dtype c_dtype, int64_t ldc, int32_t* acc_out,
                                      int64_t ld_acc, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
+
+/*
+ * tp_qgemm_w8a8_prequantized_noalloc -- tp_qgemm_w8a8_prequantized without a
+ * workspace, for callers that cannot allocate device memory (code recorded
+ * into a HIP graph, tight serving loops, harnesses that forbid allocation):
+ * the split-K partial sums of the few-row and small-grid plans go to a
+ * scratch array the library holds (32 MiB, one copy on each GPU it runs on,
+ * kept until the process ends; its address is looked up on the first call on
+ * a device). It calls no allocating routine.
+ *
+ *   qa, sa, q, w_scales, m, n, k, c, c_dtype, ldc, acc_out, ld_acc: as
+ *            tp_qgemm_w8a8_prequantized; the output bytes are the same.
+ * Errors: as tp_qgemm_w8a8_prequantized, plus TP_ERR_WORKSPACE_TOO_SMALL when
+ * the shape's partial sums (tp_workspace_size(TP_OP_QGEMM_W8A8_PREQUANTIZED,
+ * m, n, k, 0) bytes) exceed the 32 MiB, refused before any HIP call.
+ * Every call on one GPU shares its array (which keeps the last call's
+ * contents; nothing in it needs to start at zero): calls that may run at the
+ * same time on one GPU (other streams, other host threads) race and must not
+ * be issued.
+ */
+tp_status tp_qgemm_w8a8_prequantized_noalloc(const int8_t* qa, int64_t ldqa, const float* sa, const int8_t* q,
+                                             int64_t ldq, const float* w_scales, int64_t m, int64_t n, int64_t k,
+                                             void* c, tp_dtype c_dtype, int64_t ldc, int32_t* acc_out,
+                                             int64_t ld_acc, hipStream_t stream);
 
 /*
  * tp_qgemm_w8a8_prequantized_lora -- tp_qgemm_w8a8_prequantized with a LoRA

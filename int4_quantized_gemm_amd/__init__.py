@@ -227,6 +227,27 @@ def tp_qgemm_w8a8_prequantized(qa, sa, q, scales, out_dtype=torch.float32, out=N
     return out
 
 
+def tp_qgemm_w8a8_prequantized_noalloc(qa, sa, q, scales, out_dtype=torch.float32, out=None, acc=None, stream=None):
+    """tp_qgemm_w8a8_prequantized without a workspace: the split-K partial sums
+    go to the library's own scratch array (32 MiB a GPU). The caller passes the
+    output (or lets this binding allocate it with torch); the library
+    allocates nothing."""
+    ldqa = _mat(qa, "qa")
+    m, k = qa.shape
+    n = q.shape[0]
+    ldq = _mat(q, "q")
+    _vec(sa, "sa", m)
+    _vec(scales, "w_scales", n)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=qa.device)
+    ldc = _mat(out, "out")
+    ld_acc = _mat(acc, "acc") if acc is not None else 0
+    _lib.check(_lib.load().tp_qgemm_w8a8_prequantized_noalloc(qa.data_ptr(), ldqa, sa.data_ptr(), q.data_ptr(), ldq,
+                                                              scales.data_ptr(), m, n, k, out.data_ptr(), _dt(out),
+                                                              ldc, _ptr(acc), ld_acc, _stream(stream)))
+    return out
+
+
 def tp_qgemm_w8a8_prequantized_lora(qa, sa, q, scales, t, lora_b, alpha, out=None, workspace=None, stream=None):
     """C = (float(qa . q^T) * sa[m]) * s[n] + alpha * T . lora_b^T in fp32, the
     side path added in the product's store; T from tp_lora_down, lora_b bf16

@@ -58,6 +58,8 @@ SIGNATURES = {
                               _p, _p, _p, _i64, _p, _sz, _p]),
     "tp_qgemm_w8a8_prequantized": (_int, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _i64,
                                            _p, _sz, _p]),
+    "tp_qgemm_w8a8_prequantized_noalloc": (_int, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p,
+                                                   _i64, _p]),
     "tp_qgemm_w4a8": (_int, [_p, _int, _i64, _int, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _p, _p,
                              _sz, _p]),
     "tp_qgemm_w4a8_prequantized": (_int, [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _int, _i64, _p, _sz,

@@ -539,7 +539,8 @@ struct LoraIn {
 tp_status prequantized_product(int kind, const int8_t* qa, int64_t ldqa, const float* sa, const void* q, int64_t ldq,
                                const float* w_scales, int64_t m, int64_t n, int64_t k, void* c, tp_dtype c_dtype,
                                int64_t ldc, int32_t* acc_out, int64_t ld_acc, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream, const LoraIn* lora = nullptr) {
+                               size_t workspace_bytes, hipStream_t stream, const LoraIn* lora = nullptr,
+                               bool noalloc = false) {
   const bool w4 = kind == tp::GEMM_W4A8;
   const tp_op op = w4 ? TP_OP_QGEMM_W4A8_PREQUANTIZED : TP_OP_QGEMM_W8A8_PREQUANTIZED;
   if (!dtype_ok(c_dtype)) return fail(TP_ERR_UNSUPPORTED_DTYPE, "c_dtype %d is not TP_F32 or TP_BF16", (int)c_dtype);
@@ -567,7 +568,17 @@ tp_status prequantized_product(int kind, const int8_t* qa, int64_t ldqa, const f
   Extent ew;
   if (!workspace_layout(op, m, n, k, TP_A_PREROTATED, true, &wl))
     return fail(TP_ERR_SIZE_OVERFLOW, "workspace size overflows");
-  TP_TRY(check_workspace(wl, workspace, workspace_bytes, &ew));
+  if (noalloc) {
+    // the library's own scratch array instead of a workspace (no overlap with
+    // any caller buffer possible)
+    if (wl.total > tp::NOALLOC_SCRATCH_BYTES)
+      return fail(TP_ERR_WORKSPACE_TOO_SMALL,
+                  "this shape needs %lld bytes of split-K partial sums; the no-allocation entry point holds %lld "
+                  "(use tp_qgemm_w8a8_prequantized with a workspace)",
+                  (long long)wl.total, (long long)tp::NOALLOC_SCRATCH_BYTES);
+  } else {
+    TP_TRY(check_workspace(wl, workspace, workspace_bytes, &ew));
+  }
   const Extent* ins[] = {&eqa, &esa, &eq, &es, &et, &eb};
   for (const Extent* i : ins)
     if (overlaps(ec, *i) || overlaps(eacc, *i) || overlaps(ew, *i))
@@ -592,6 +603,7 @@ tp_status prequantized_product(int kind, const int8_t* qa, int64_t ldqa, const f
   g.acc_out = acc_out;
   g.ld_acc = ld_acc;
   g.part = wl.total > 0 ? workspace : nullptr;
+  if (noalloc && wl.total > 0) TP_TRY(hip_status(tp::noalloc_scratch(&g.part), "scratch address"));
   if (lora) {
     g.lora.t = lora->t;
     g.lora.b = (const uint16_t*)lora->b;
@@ -618,6 +630,14 @@ tp_status tp_qgemm_w8a8_prequantized(const int8_t* qa, int64_t ldqa, const float
                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return prequantized_product(tp::GEMM_W8A8, qa, ldqa, sa, q, ldq, w_scales, m, n, k, c, c_dtype, ldc, acc_out,
                               ld_acc, workspace, workspace_bytes, stream);
+}
+
+tp_status tp_qgemm_w8a8_prequantized_noalloc(const int8_t* qa, int64_t ldqa, const float* sa, const int8_t* q,
+                                             int64_t ldq, const float* w_scales, int64_t m, int64_t n, int64_t k,
+                                             void* c, tp_dtype c_dtype, int64_t ldc, int32_t* acc_out,
+                                             int64_t ld_acc, hipStream_t stream) {
+  return prequantized_product(tp::GEMM_W8A8, qa, ldqa, sa, q, ldq, w_scales, m, n, k, c, c_dtype, ldc, acc_out,
+                              ld_acc, nullptr, 0, stream, nullptr, true);
 }
 
 tp_status tp_qgemm_w8a8_prequantized_lora(const int8_t* qa, int64_t ldqa, const float* sa, const int8_t* q,

@@ -18,6 +18,7 @@
 // Rows past M or N are clamped on load and masked on store; K needs no tail
 // (k % 256 == 0).
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -171,6 +172,32 @@ static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
       return launch_pp<KIND, 128, 192, 64, 48, 5>(g, stream, 4, pl.splits, pl.sps);
   }
   return hipErrorInvalidValue;
+}
+
+// The no-allocation entry point's split-K partial sums. In host code the
+// array's name stands for a host-side shadow, not a device address: the
+// address each device holds it at comes from hipGetSymbolAddress, called once
+// per device with that device current, and only that address is passed on.
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_qgemm(const GemmArgs& g, hipStream_t stream) {

@@ -79,4 +79,11 @@ void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn)
 // product runs unsplit); -1 when the size overflows.
 int64_t qgemm_partial_bytes(int kind, int64_t m, int64_t n, int64_t k);
 
+// Scratch memory of the no-allocation entry point: a file-scope device array
+// of NOALLOC_SCRATCH_BYTES in gemm.hip, one copy per GPU the library runs on
+// (held until the process ends). noalloc_scratch returns its device address
+// on the current device, looked up once per device.
+constexpr int64_t NOALLOC_SCRATCH_BYTES = (int64_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace tp

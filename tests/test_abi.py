@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.tp_abi_version() == 7
+    assert lib.tp_abi_version() == 8
     for code, name in _lib.STATUS_NAMES.items():
         assert lib.tp_status_string(code).decode() == name
 
@@ -260,6 +260,33 @@ def pq(lib, qa=A, ldqa=512, sa=C, q=B, ldq=512, s=C + 4096, m=64, n=256, k=512, 
 ])
 def test_prequantized_refusals(lib, kw, status):
     assert pq(lib, **kw) == status, _err(lib)
+
+
+def pqn(lib, qa=A, ldqa=512, sa=C, q=B, ldq=512, s=C + 4096, m=64, n=256, k=512, c=D, cd=0, ldc=256, acc=0,
+        ld_acc=0):
+    return lib.tp_qgemm_w8a8_prequantized_noalloc(qa, ldqa, sa, q, ldq, s, m, n, k, c, cd, ldc, acc or None, ld_acc,
+                                                  None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    # 64 x 49152 x 3072 needs 36 MiB of split-K partial sums: more than the
+    # 32 MiB scratch array, refused before any HIP call
+    (dict(n=49152, k=3072, ldqa=3072, ldq=3072, ldc=49152, s=C + (1 << 20)), 9),
+    (dict(qa=0), 1),
+    (dict(c=0), 1),
+    (dict(k=300, ldqa=512, ldq=512), 3),
+    (dict(ldc=200), 4),
+    (dict(cd=3), 6),
+    (dict(c=A + 256), 10),             # c overlaps qa
+])
+def test_prequantized_noalloc_refusals(lib, kw, status):
+    assert pqn(lib, **kw) == status, _err(lib)
+    assert _err(lib)
+
+
+def test_prequantized_noalloc_empty_is_noop(lib):
+    assert pqn(lib, m=0) == 0
+    assert pqn(lib, n=0) == 0
 
 
 def test_prequantized_large_m_needs_no_workspace(lib):
