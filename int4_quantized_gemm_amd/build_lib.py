@@ -59,5 +59,35 @@ def build(verbose=False):
     return LIB
 
 
+def build_sanitized_api(outdir, verbose=False):
+    """A host-sanitized copy of the library for the CPU tests of the C ABI:
+    api.cpp (host code only) built with g++ under AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the HIP objects of the last build()
+    (no GPU code is built with a sanitizer). Returns the .so path; a Python
+    process loads it with the sanitizer runtime preloaded."""
+    objs = [os.path.join(BUILD, s + ".o") for s in SOURCES if s.endswith(".hip")]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise FileNotFoundError("run build() first; missing " + ", ".join(missing))
+    os.makedirs(outdir, exist_ok=True)
+    api_o = os.path.join(outdir, "api_sanitized.o")
+    lib = os.path.join(outdir, "libtp_sanitized.so")
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
+    steps = [
+        ["g++", "-O1", "-g", "-std=c++17", "-fPIC"] + san + ["-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+                                                             "-I", os.path.join(ROOT, "include"), "-c",
+                                                             os.path.join(CSRC, "api.cpp"), "-o", api_o],
+        ["g++", "-shared"] + san + ["-o", lib, api_o] + objs + ["-L/opt/rocm/lib", "-lamdhip64",
+                                                                "-Wl,-rpath,/opt/rocm/lib"],
+    ]
+    for cmd in steps:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(" ".join(cmd[:2]) + " failed:\n" + r.stdout + r.stderr)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
