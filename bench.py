@@ -209,6 +209,33 @@ def cpu_baseline(rows):
 
 
 # ------------------------------------------------------- M <= 64 sweep (HBM)
+def _graph_times(torch, fn, copies):
+    """Median and min seconds per call of fn(i) over i = 0 .. copies-1, the
+    calls captured in one HIP graph and replayed (5 repeats of at least 64
+    calls), so the time is the GPU's, not the Python launch rate's."""
+    for i in range(copies):
+        fn(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(copies):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(2, -(-64 // copies))
+    med = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        med.append(e0.elapsed_time(e1) / (reps * copies) * 1e-3)
+    del graph
+    return float(np.median(med)), float(np.min(med))
+
+
 def small_m_sweep(args, emit=False):
     """Products with 1, 16 and 64 activation rows against the full-size
     weights of the step. They are bound by reading the weights, so each case
@@ -251,29 +278,7 @@ def small_m_sweep(args, emit=False):
                 fn = lambda i, g=g: g(xr, qs[i][0], qs[i][1], rotate=False, out=out, workspace=ws)
                 abytes = m * wl.k * 2
             nbytes = wbytes + abytes + out.numel() * out.element_size()
-            # One graph replays a call on every weight copy: the timing is
-            # then the GPU's, not the Python launch rate's.
-            for i in range(copies):
-                fn(i)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for i in range(copies):
-                    fn(i)
-            graph.replay()
-            torch.cuda.synchronize()
-            reps = max(2, -(-64 // copies))
-            med = []
-            for _ in range(5):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(reps):
-                    graph.replay()
-                e1.record()
-                torch.cuda.synchronize()
-                med.append(e0.elapsed_time(e1) / (reps * copies) * 1e-3)
-            del graph
-            t_med, t_min = float(np.median(med)), float(np.min(med))
+            t_med, t_min = _graph_times(torch, fn, copies)
             gbs = nbytes / t_med / 1e9
             row = {"case": f"{kind}[{wl.name}]", "m": m, "n": wl.n, "k": wl.k, "bytes": nbytes,
                    "us_median": round(t_med * 1e6, 2), "us_min": round(t_min * 1e6, 2), "gbs": round(gbs, 1),
@@ -338,6 +343,18 @@ def next_rows(args, cpu):
         alg = 2 * w.m * w.k * es + out_bytes
         us = _time_us(torch, fused)
         us2 = _time_us(torch, second)
+        # The unfused path as it would run: torch's SwiGLU (silu, multiply,
+        # rounding to bf16: three elementwise kernels) then the second pass.
+        tmp = torch.empty((w.m, w.k), dtype=g.dtype, device=d)
+        hb = torch.empty((w.m, w.k), dtype=torch.bfloat16, device=d)
+
+        def unfused(second_on=(lambda hh: tp.tp_quantize_rows_int8(hh, qa=y, sa=sc)) if w.out == "i8" else
+                    (lambda hh: tp.tp_hadamard_rotate_rows(hh, out=y))):
+            torch.mul(torch.nn.functional.silu(g), u, out=tmp)
+            hb.copy_(tmp)
+            second_on(hb)
+
+        us3 = _time_us(torch, unfused)
         silu_pass_us = (2 * w.m * w.k * es + w.m * w.k * 2) / (PEAK_HBM_GBS * 1e3)
         row = {"row": "ffn_middle", "workload": f"{w.name}: M={w.m}, K={w.k}, {w.in_dtype} gate/up -> {w.out}",
                "us": round(us, 2), "roofline": {"bound": "hbm", "achieved": round(alg / us / 1e3, 1),
@@ -346,8 +363,11 @@ def next_rows(args, cpu):
                                                 "algorithmic_bytes": alg},
                "unfused_us": round(silu_pass_us + us2, 2),
                "unfused_note": f"ideal SwiGLU pass at peak HBM ({silu_pass_us:.1f} us) + measured rotation pass over "
-                               f"bf16 h ({us2:.1f} us, {second_bytes / us2 / 1e3:.0f} GB/s)"}
-        del gu, g, u, h, y
+                               f"bf16 h ({us2:.1f} us, {second_bytes / us2 / 1e3:.0f} GB/s)",
+               "unfused_measured_us": round(us3, 2),
+               "unfused_measured_note": "torch SwiGLU (silu, multiply, bf16 rounding) then the same second pass, "
+                                        "timed the same way"}
+        del gu, g, u, h, y, tmp, hb
         if cpu:
             rows = 256
             g64, u64 = (t.double().numpy() for t in W.gate_up(w, rows=rows))
