@@ -34,10 +34,12 @@ namespace tp {
 //          four code fragments widened in the memory phase (5-7% faster than
 //          all in the compute phase, where a wave's VALU work serializes with
 //          its own MFMAs; 1.7% faster than all four early);
-//   W8A8   256x256 (128x64 waves), 4 stages, or 256x192 (64x96 waves) when
-//          its rounds of tiles, at 0.825 of a 256x256 tile's time each, take
-//          less (N = 3072 at M = 4096: one full round of 256 tiles instead of
-//          192 tiles; N = 9216: 3 full rounds instead of 2.25);
+//   W8A8   256x256 (128x64 waves), 4 stages, or 256x192 (64x96 waves) or
+//          256x288 (64x144 waves) when their rounds of tiles, at 0.825 and
+//          1.125 of a 256x256 tile's time each, take less (N = 3072 at
+//          M = 4096: one full round of 256x192 tiles instead of 192 tiles of
+//          256x256; N = 9216: 2 full rounds of 256x288 tiles instead of 2.25
+//          of 256x256);
 //   W4     256x192 (128x48 waves), 3 stages, when that grid has at least 192
 //          tiles (4032x3072 splits into exactly 256): 128-row waves spread
 //          the widening of each code over 8 MFMAs (measured 4032x3072x12288:
@@ -56,7 +58,7 @@ namespace tp {
 // (pp_map_tile): 4 for W8, W4 and wide W8A8 outputs, 8 otherwise (measured:
 // W8 4096x3072x12288 307 -> 257 us from 8 to 4).
 // Smaller outputs: see pick_plan.
-enum KernelCfg { CFG_PP_256x256 = 1, CFG_PP_128x192 = 2, CFG_PP_256x192 = 3, CFG_PP_256x128 = 4 };
+enum KernelCfg { CFG_PP_256x256 = 1, CFG_PP_128x192 = 2, CFG_PP_256x192 = 3, CFG_PP_256x128 = 4, CFG_PP_256x288 = 5 };
 constexpr int64_t W4_MIN_WIDE_TILES = 192;
 constexpr int64_t NUM_CUS = 256;
 
@@ -80,11 +82,16 @@ static PpPlan pick_plan(int kind, int64_t m, int64_t n, int64_t k) {
     if (kind == GEMM_W8A8) {
       // Rounds of tiles on the CUs, weighted by a tile's time: a 256x192 tile
       // (64x96 waves) takes about 0.825 of a 256x256 one (0.75 of the area at
-      // a lower rate). 4096x9216: 3 rounds of 256x256 (the last a quarter
-      // full) against 3 of 256x192, 131 -> 119 us.
+      // a lower rate), a 256x288 tile (64x144 waves) about 1.125 (its area).
+      // 4096x9216: 2.25 rounds of 256x256 (3, the last a quarter full), 3 of
+      // 256x192 (2.475) or 2 of 256x288 (2.25): 138 -> 123.5 us from 256x192
+      // to 256x288 (same box).
       const int64_t r256 = (big + NUM_CUS - 1) / NUM_CUS;
       const int64_t r192 = (((m + 255) / 256) * ((n + 191) / 192) + NUM_CUS - 1) / NUM_CUS;
-      if (r192 * 33 < r256 * 40) return PpPlan{CFG_PP_256x192, 1, 0};
+      const int64_t r288 = (((m + 255) / 256) * ((n + 287) / 288) + NUM_CUS - 1) / NUM_CUS;
+      const int64_t c256 = r256 * 320, c192 = r192 * 264, c288 = r288 * 360;  // rounds x 320 x relative tile time
+      if (c288 < c256 && c288 < c192) return PpPlan{CFG_PP_256x288, 1, 0};
+      if (c192 < c256) return PpPlan{CFG_PP_256x192, 1, 0};
     }
     return PpPlan{CFG_PP_256x256, 1, 0};
   }
@@ -111,6 +118,7 @@ void qgemm_tile_for(int kind, int64_t m, int64_t n, int64_t k, int* bm, int* bn)
   switch (pick_cfg(kind, m, n, k)) {
     case CFG_PP_256x256: *bm = 256; *bn = 256; return;
     case CFG_PP_256x192: *bm = 256; *bn = 192; return;
+    case CFG_PP_256x288: *bm = 256; *bn = 288; return;
     case CFG_PP_256x128: *bm = 256; *bn = 128; return;
     default: *bm = 128; *bn = 192; return;
   }
@@ -163,6 +171,14 @@ static hipError_t launch_kind(const GemmArgs& g, hipStream_t stream) {
     case CFG_PP_256x192:
       if constexpr (KIND == GEMM_W8A8) return launch_pp<KIND, 256, 192, 64, 96, 4>(g, stream);
       if constexpr (KIND == GEMM_W4) return launch_pp<KIND, 256, 192, 128, 48, 3, 2>(g, stream, 4);
+      break;
+    case CFG_PP_256x288:
+      // The side path in the store needs registers this tile does not leave
+      // (its instance spills): such calls take 256x192 tiles.
+      if constexpr (KIND == GEMM_W8A8) {
+        if (g.lora.t) return launch_pp<KIND, 256, 192, 64, 96, 4>(g, stream);
+        return launch_pp<KIND, 256, 288, 64, 144, 4>(g, stream);
+      }
       break;
     case CFG_PP_256x128:
       if constexpr (KIND == GEMM_W4A8) return launch_pp<KIND, 256, 128, 128, 32, 5, 2>(g, stream, 4);

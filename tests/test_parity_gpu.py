@@ -402,11 +402,12 @@ def test_w8a8_dit_block_sampled(name):
     _w8a8_case(wl, row_sel=sample_rows(wl.m, 40, seed=wl.seed))
 
 
-@pytest.mark.parametrize("m,n,k", [(4000, 9000, 1024), (4000, 24000, 512)])
+@pytest.mark.parametrize("m,n,k", [(4000, 9000, 1024), (4000, 3000, 1024), (4000, 24000, 512)])
 def test_w8a8_large_ragged(m, n, k):
-    """Ragged M and N on the large-tile paths: 4000x9000 takes 256x192 tiles
-    (3 full rounds against 2.25 of 256x256), 4000x24000 256x256 tiles. Sampled
-    rows include the last tile-row's tail."""
+    """Ragged M and N on the large-tile paths: 4000x9000 takes 256x288 tiles
+    (2 full rounds against 2.25 of 256x256), 4000x3000 256x192 tiles (one
+    round), 4000x24000 256x256 tiles. Sampled rows include the last tile-row's
+    tail."""
     announce("tp_qgemm_w8a8 large ragged", m, n, k)
     wl = W.TINY.with_(name=f"ragged{m}x{n}", m=m, n=n, k=k, seed=m + n, act_outliers=3, w_outliers=3, path="w8a8")
     _w8a8_case(wl, row_sel=sample_rows(m, 24, seed=n))
