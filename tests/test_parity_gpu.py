@@ -413,6 +413,42 @@ def test_w8a8_large_ragged(m, n, k):
     _w8a8_case(wl, row_sel=sample_rows(m, 24, seed=n))
 
 
+@pytest.mark.parametrize("m,n,k", [(1024, 3072, 1024), (600, 1000, 1024), (2000, 5184, 1024), (4096, 9216, 256)])
+def test_w8a8_large_output_views(m, n, k):
+    """The multi-stage W8A8 epilogue on dense and padded outputs: the int32
+    accumulators are exact, the fp32 output is (float(acc) * sa) * s rounded
+    as written, an output view with odd row pitches and a base 4 bytes past a
+    16-byte boundary gets the same bytes and nothing outside the view, and
+    the bf16 output (dense or padded) is the RNE rounding of the fp32 one.
+    Shapes: 128x192 tiles, a ragged 600x1000 split along K (partial sums),
+    256x192 tiles and 256x288 tiles (4096x9216)."""
+    d = dev()
+    announce("tp_qgemm_w8a8_prequantized output views", m, n, k)
+    g = torch.Generator().manual_seed(m + n)
+    qa = torch.randint(-127, 128, (m, k), dtype=torch.int8, generator=g).to(d)
+    q = torch.randint(-127, 128, (n, k), dtype=torch.int8, generator=g).to(d)
+    sa = (torch.rand(m, generator=g) + 0.5).to(d)
+    s = (torch.rand(n, generator=g) + 0.5).to(d)
+    acc = torch.empty((m, n), dtype=torch.int32, device=d)
+    y = tp.tp_qgemm_w8a8_prequantized(qa, sa, q, s, acc=acc)
+    racc = (qa.cpu().to(torch.float64) @ q.cpu().to(torch.float64).T).to(torch.int64)  # exact: |sum| < 2^53
+    assert torch.equal(acc.cpu().to(torch.int64), racc), "int32 accumulators differ"
+    ref = (racc.to(torch.float32) * sa.cpu()[:, None]) * s.cpu()[None, :]
+    assert torch.equal(y.cpu(), ref), "fp32 output is not (float(acc) * sa) * s"
+    # odd pitches and a base 4 bytes past a 16-byte boundary
+    ybuf = torch.full((m, n + 3), -1.0, dtype=torch.float32, device=d)
+    abuf = torch.full((m, n + 5), -1, dtype=torch.int32, device=d)
+    yv = tp.tp_qgemm_w8a8_prequantized(qa, sa, q, s, out=ybuf[:, 1:n + 1], acc=abuf[:, 1:n + 1])
+    assert torch.equal(yv, y) and torch.equal(abuf[:, 1:n + 1], acc)
+    assert bool((ybuf[:, 0] == -1).all()) and bool((ybuf[:, n + 1:] == -1).all()), "stores outside the view"
+    assert bool((abuf[:, 0] == -1).all()) and bool((abuf[:, n + 1:] == -1).all()), "stores outside the view"
+    ybf = tp.tp_qgemm_w8a8_prequantized(qa, sa, q, s, out_dtype=torch.bfloat16)
+    assert torch.equal(ybf, y.to(torch.bfloat16)), "bf16 output is not the RNE rounding of the fp32 one"
+    bbuf = torch.zeros((m, n + 1), dtype=torch.bfloat16, device=d)
+    ybv = tp.tp_qgemm_w8a8_prequantized(qa, sa, q, s, out=bbuf[:, :n])
+    assert torch.equal(ybv, ybf)
+
+
 @pytest.mark.parametrize("kind,m,n,k", [("w8", 3000, 5000, 512), ("w4", 4000, 3100, 1024)])
 def test_weight_only_large_ragged(kind, m, n, k):
     """Ragged M and N on the large-tile paths (W8 256x256, W4 256x192), with
