@@ -9,8 +9,9 @@
 //  * k_rotq_rows<I4_GRP> rotate in fp64, then int4 with one scale per
 //                        (row, 256-group), packed two per byte (the "-q4" width
 //                        of section "幅とメモリ").
-//  * k_rotq_i8_fast      the int8 rows of k_rotq_rows<I8_ROW> in fp32 with an
-//                        exact fallback.
+//  * k_rotq_i8_d         the int8 rows of k_rotq_rows<I8_ROW> for up to 48
+//                        groups a row, 16 lanes a group (the same fp64
+//                        transform; several groups of a row in flight).
 //
 //  * k_unrotate_rows     y = (q * s) . blockdiag(H/16) in fp64 (exact), rounded
 //                        once: undoing a rotated, quantized weight (section
@@ -162,65 +163,13 @@ __global__ __launch_bounds__(256) void k_rotq_rows(Src src, int64_t rows, int gr
   }
 }
 
-// ------------------------------- rotate and quantize rows to int8 (fast path)
-// The same codes and scales as k_rotq_rows<MODE_I8_ROW>, computed in fp32 with
-// a proven error bound and redone exactly (fp64) only where the bound cannot
-// decide.
-//
-// Layout: a 256-group is held by one 16-lane row of the wave. Lane l loads
-// elements 16 l + i (i = 0..15, index bits 0-3 in registers) and applies the
-// four butterfly stages of those bits; the row then transposes the group
-// through LDS so that lane l holds elements l + 16 r (bits 4-7 in registers)
-// and applies the other four stages. Outputs stay in that order; the codes go
-// back through LDS to be stored 16 contiguous bytes per lane.
-//
-// Error bound (unnormalized transform, fp32 round-to-nearest): the rounding
-// errors that reach one output are those of the nodes of its butterfly tree;
-// at each of the 8 stages these nodes partition the 256 inputs, so each stage
-// adds at most 2^-24 * L1 (L1 = sum of |inputs| of the group) and the output
-// error is at most 8 * 2^-24 * L1 = 2^-21 L1 (before the exact 1/16).
-//   * Row maximum: elements whose fp32 magnitude is within twice the largest
-//     bound of the fp32 maximum are the only ones that can be the true
-//     maximum; their groups are transformed again in fp64 (exact for these
-//     inputs, as in k_rotq_rows) and the scale comes from the exact maximum.
-//   * Codes: t = v * (1/(16 s)) in fp32 is within B / (16 s) + 2^-22 (|t| + 1)
-//     of the exact quotient; a code whose t is at least that far from every
-//     half-integer rounds the same way as the exact one. A group with a code
-//     closer than that is redone in fp64 with quant_code (the reference rule).
-
-template <int M>
-__device__ __forceinline__ int dpp_xor(int v) {
-  if constexpr (M == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-  if constexpr (M == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-  if constexpr (M == 4)  // half mirror (i ^ 7), then quad reverse (i ^ 3)
-    return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF, false);
-  if constexpr (M == 8)  // mirror (i ^ 15), then half mirror (i ^ 7)
-    return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false), 0x141, 0xF, 0xF, false);
-  return v;
-}
-
-template <int M>
-__device__ __forceinline__ float xor16(float v) {
-  return __builtin_bit_cast(float, dpp_xor<M>(__builtin_bit_cast(int, v)));
-}
-
-// Sum over the 16 lanes of a row (every lane gets the total).
-__device__ __forceinline__ float sum16(float v) {
-  v += xor16<1>(v);
-  v += xor16<2>(v);
-  v += xor16<4>(v);
-  v += xor16<8>(v);
-  return v;
-}
-
-// Bitwise or over the 16 lanes of a row (every lane gets the result).
-__device__ __forceinline__ uint32_t or16(uint32_t v) {
-  v |= (uint32_t)dpp_xor<1>((int)v);
-  v |= (uint32_t)dpp_xor<2>((int)v);
-  v |= (uint32_t)dpp_xor<4>((int)v);
-  v |= (uint32_t)dpp_xor<8>((int)v);
-  return v;
-}
+// --------------------------------------------- group layout of the int8 rows
+// A 256-group is held by one 16-lane row of the wave: lane l loads elements
+// 16 l + i (i = 0..15, index bits 0-3 in registers) and applies the four
+// butterfly stages of those bits; the row then transposes the group through
+// LDS so that lane l holds elements l + 16 r (bits 4-7 in registers) and
+// applies the other four stages. Outputs stay in that order; the codes go back
+// through LDS to be stored 16 contiguous bytes per lane.
 
 // Four butterfly stages over the register index of 16 values.
 template <typename T>
@@ -257,8 +206,7 @@ __device__ __forceinline__ void transpose16(T (&v)[16], T* buf, int l16) {
   for (int r = 0; r < 16; ++r) v[r] = buf[l16 + (16 + PAD) * r];
 }
 
-// The 16 inputs of one lane for one group, kept as loaded (bf16 pairs or fp32)
-// for the exact fallbacks.
+// The 16 inputs of one lane for one group, as loaded (bf16 pairs or fp32).
 template <typename TIn>
 struct Raw16;
 
@@ -296,25 +244,21 @@ struct Raw16<float> {
 
 // ------------------------------------------------------------- input sources
 // A source yields 8 or 16 consecutive elements of a row: as fp32 (load8), as
-// fp64 (load8d), or as the raw words the fast int8 kernel keeps for its exact
-// fallbacks (load16, into Raw16<raw_elem>).
+// fp64 (load8d), or as raw words (fetch then finish, into Raw16<raw_elem>)
+// for the int8 rows.
 
 // Rows of a [rows, k] buffer of fp32 or bf16 (uint16_t) elements.
 template <typename T>
 struct RowSrc {
   typedef T raw_elem;
-  // The fast int8 kernel may load a group's inputs again for its exact
-  // fallbacks instead of keeping them in registers.
-  static constexpr bool REREAD = true;
   const T* x;
   int64_t ldx;
   __device__ __forceinline__ void load8(int64_t r, int64_t c, float (&v)[8]) const { tp::load8(x + r * ldx + c, v); }
   __device__ __forceinline__ void load8d(int64_t r, int64_t c, double (&v)[8]) const {
     tp::load8d(x + r * ldx + c, v);
   }
-  __device__ __forceinline__ void load16(int64_t r, int64_t c, Raw16<T>& raw) const { raw.load(x + r * ldx + c); }
-  // Two-phase form of load16: fetch issues the loads, finish produces the
-  // raw words (here the loaded words themselves).
+  // Two-phase load of 16 elements for the int8 rows: fetch issues the loads,
+  // finish produces the raw words (here the loaded words themselves).
   typedef Raw16<T> stash_t;
   __device__ __forceinline__ void fetch(int64_t r, int64_t c, stash_t& st) const { st.load(x + r * ldx + c); }
   __device__ __forceinline__ void finish(int64_t, int64_t, const stash_t& st, Raw16<T>& raw) const { raw = st; }
@@ -326,7 +270,6 @@ struct RowSrc {
 template <int BITS>
 struct DequantSrc {
   typedef float raw_elem;
-  static constexpr bool REREAD = false;
   const uint8_t* q;
   int64_t ldq;  // bytes
   const float* s;
@@ -393,7 +336,6 @@ __device__ __noinline__ uint32_t swiglu_exact(float g, float u) {
 template <typename T>
 struct SwigluSrc {
   typedef uint16_t raw_elem;
-  static constexpr bool REREAD = false;  // h is computed, not loaded: keep it
   const T* g;
   int64_t ldg;
   const T* u;
@@ -451,14 +393,9 @@ struct SwigluSrc {
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = (double)f[j];
   }
-  __device__ __forceinline__ void load16(int64_t r, int64_t c, Raw16<uint16_t>& raw) const {
-    uint32_t hb[16];
-    bits(r, c, hb);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) raw.w[i] = hb[2 * i] | (hb[2 * i + 1] << 16);
-  }
-  // Two-phase form of load16: fetch issues the loads of g and u, finish
-  // computes h (so a kernel can have several groups' loads in flight).
+  // Two-phase load of 16 elements for the int8 rows: fetch issues the loads of
+  // g and u, finish computes h (so a kernel can have several groups' loads in
+  // flight).
   struct stash_t {
     Raw16<T> g, u;
   };
@@ -480,73 +417,34 @@ struct SwigluSrc {
   }
 };
 
-template <int M>
-__device__ __forceinline__ double xor16d(double v) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)dpp_xor<M>((int)(uint32_t)u);
-  const uint32_t hi = (uint32_t)dpp_xor<M>((int)(uint32_t)(u >> 32));
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
-// Exact (fp64) unnormalized rotated element e of a group, summed over the 16
-// lanes of the row (lane l holds inputs 16 l .. 16 l + 15 in raw): the sign of
-// input i is (-1)^popcount(i & e). Without rotation, input e itself. Every
-// lane of the row must be active; all get the value.
-template <typename TIn>
-__device__ __forceinline__ double exact_elem(const Raw16<TIn>& raw, bool rotate, int e, int l16) {
-  double acc = 0.0;
-  if (rotate) {
-    // Bit i of w: the parity of popcount((16 l16 + i) & e), i.e. the sign of
-    // input i of this lane. The parity is linear in e, so the low half is the
-    // xor of the Walsh rows of e's low bits (0xAAAA for bit 0, 0xCCCC, 0xF0F0,
-    // 0xFF00) and the lane's part flips all sixteen.
-    const int el = e & 15;
-    uint32_t w = ((el & 1) ? 0xAAAAu : 0u) ^ ((el & 2) ? 0xCCCCu : 0u) ^ ((el & 4) ? 0xF0F0u : 0u) ^
-                 ((el & 8) ? 0xFF00u : 0u);
-    if (__builtin_popcount((unsigned)(l16 & (e >> 4))) & 1) w ^= 0xFFFFu;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint64_t xb = __builtin_bit_cast(uint64_t, (double)raw.get(i));
-      acc += __builtin_bit_cast(double, xb ^ ((uint64_t)((w >> i) & 1u) << 63));
-    }
-  } else {
-    // input e lives in lane e / 16, register e % 16
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i == (e & 15)) acc = (double)raw.get(i);
-    acc = (l16 == (e >> 4)) ? acc : 0.0;
-  }
-  acc += xor16d<1>(acc);
-  acc += xor16d<2>(acc);
-  acc += xor16d<4>(acc);
-  acc += xor16d<8>(acc);
-  return acc;
-}
-
-constexpr int RQ_ROW_BYTES = 1280 + 64;  // LDS per 16-lane row: 256 padded floats
-constexpr float RQ_MAGIC = 12582912.0f;  // 1.5 * 2^23: adding it rounds to an integer (RNE)
-
-// WPR = 1: one wave per row, four rows per block (k <= 12 * 256).
-// WPR = 4: one block per row, the four waves split the groups (k <= 48 * 256).
-// Sources that are plain rows (REREAD) load a group's inputs again for the
-// rare exact fallbacks, which fits the kernel in 128 registers: four waves per
-// SIMD, so the 4096 one-wave rows of a 4096 x 3072 input are all resident at
-// once. Computed sources (SwiGLU) keep their inputs in registers for the
-// fallbacks, within the 168 registers of three waves per SIMD.
-template <typename Src, int WPR, int WPE = Src::REREAD ? 4 : 3>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k_rotq_i8_fast(
+// ------------------------- rotate and quantize rows to int8 (fp64 transform)
+// The same codes and scales as k_rotq_rows<MODE_I8_ROW> (the transform in
+// fp64, whose values are the exact ones whenever k_rotq_rows' are: every stage
+// only adds or subtracts), on the group layout above: a 16-lane row of the
+// wave per 256-group, 16 elements a lane, a row transpose through LDS between
+// the butterflies of index bits 0-3 and 4-7. The row maximum and the codes are
+// read off the exact values directly.
+//
+// Code of an element v (unnormalized, 16 x the rotation): f = fma(v, invu,
+// 1.5 * 2^52) holds in its low bits the integer nearest the exact product v *
+// invu (invu = (1/s) / 16, exact from 1/s), and d = fma(v, invu, 1.5 * 2^52 -
+// f) its distance from that integer. The product is within 2^-45 of the exact
+// quotient, so when |d| < 0.5 - 1e-9 the quotient rounds to the same integer,
+// which is what quant_code gives; the rare others take quant_code itself, as
+// do rows whose scale is subnormal (see below).
+template <typename Src, int WPR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_rotq_i8_d(
     Src src, int64_t rows, int groups, int rotate, int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales) {
   typedef typename Src::raw_elem TIn;
-  constexpr bool KEEP = !Src::REREAD;
-  constexpr int NU = 3;  // groups per 16-lane set
+  constexpr int NU = 3;   // groups per 16-lane row
   constexpr int NWB = 4;  // waves per block
+  constexpr int ROWB = 16 * (16 + 2) * 8;  // one row's transpose buffer (transpose16<double>'s padded layout)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int set = lane >> 4, l16 = lane & 15;
-  __shared__ __align__(16) uint8_t lds[4 * NWB * RQ_ROW_BYTES];
-  __shared__ float red[2][NWB];
+  __shared__ __align__(16) uint8_t lds[NWB * 4 * ROWB];
   __shared__ double red64[NWB];
-  uint8_t* mybuf = lds + (wave * 4 + set) * RQ_ROW_BYTES;
-  float* fbuf = reinterpret_cast<float*>(mybuf);
+  double* dbuf = reinterpret_cast<double*>(lds + (wave * 4 + set) * ROWB);
+  uint8_t* bbuf = lds + (wave * 4 + set) * ROWB;
   int64_t row;
   int gb, ge;
   if constexpr (WPR == 1) {
@@ -561,198 +459,86 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     ge = min(groups, gb + gpw);
   }
 
-  // Load every group of this wave (up to 3 per 16-lane row) and transform it.
-  Raw16<TIn> raw[KEEP ? NU : 1];  // the inputs, kept for the exact fallbacks
-  float v[NU][16];
-  float bnd[NU];
   bool has[NU];
-  {
-    typename Src::stash_t st[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      has[u] = gb + set + 4 * u < ge;
-      if (has[u]) src.fetch(row, (int64_t)(gb + set + 4 * u) * 256 + l16 * 16, st[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      Raw16<TIn> r0;
-      if (has[u])
-        src.finish(row, (int64_t)(gb + set + 4 * u) * 256 + l16 * 16, st[u], r0);
-      else
-        r0.zero();
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[u][i] = r0.get(i);
-      if constexpr (KEEP) raw[u] = r0;
-    }
-  }
-  // The inputs of unit U for an exact fallback (every lane of the row takes
-  // part; lanes without the group read zeros).
-  auto inputs = [&](auto uc) -> Raw16<TIn> {
-    constexpr int U = decltype(uc)::value;
-    if constexpr (KEEP) {
-      return raw[U];
-    } else {
-      Raw16<TIn> r;
-      if (has[U])
-        src.load16(row, (int64_t)(gb + set + 4 * U) * 256 + l16 * 16, r);
-      else
-        r.zero();
-      return r;
-    }
-  };
-  float amax = 0.f, bmax = 0.f;
-  float umax[NU];  // this lane's largest |value| of each unit
+  typename Src::stash_t st[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    bnd[u] = 0.f;
+    has[u] = gb + set + 4 * u < ge;
+    if (has[u]) src.fetch(row, (int64_t)(gb + set + 4 * u) * 256 + l16 * 16, st[u]);
+  }
+  double v[NU][16];
+  double amax = 0.0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    Raw16<TIn> r0;
+    if (has[u])
+      src.finish(row, (int64_t)(gb + set + 4 * u) * 256 + l16 * 16, st[u], r0);
+    else
+      r0.zero();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[u][i] = (double)r0.get(i);
     if (rotate) {
-      float l1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) l1 += fabsf(v[u][i]);
-      l1 = sum16(l1);  // rows without a group hold zeros
       fwht16_regs(v[u]);
-      transpose16(v[u], fbuf, l16);
+      transpose16(v[u], dbuf, l16);
       fwht16_regs(v[u]);
-      bnd[u] = l1 * 0x1.00004p-21f;  // 2^-21 L1, rounded up
     } else {
-      transpose16(v[u], fbuf, l16);
+      transpose16(v[u], dbuf, l16);  // the same output order either way
     }
-    umax[u] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) umax[u] = fmaxf(umax[u], fabsf(v[u][i]));
-    amax = fmaxf(amax, umax[u]);
-    bmax = fmaxf(bmax, bnd[u]);
+    for (int i = 0; i < 16; ++i) amax = fmax(amax, fabs(v[u][i]));
+    __builtin_amdgcn_sched_barrier(0);  // one group at a time: the next one's registers are not live yet
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-  bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-  bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+  amax = wave_max(amax);  // rows without a group hold zeros
   if constexpr (WPR > 1) {
-    if (lane == 0) {
-      red[0][wave] = amax;
-      red[1][wave] = bmax;
-    }
+    if (lane == 0) red64[wave] = amax;
     __syncthreads();
-    amax = red[0][0];
-    bmax = red[1][0];
+    amax = red64[0];
 #pragma unroll
-    for (int w = 1; w < WPR; ++w) {
-      amax = fmaxf(amax, red[0][w]);
-      bmax = fmaxf(bmax, red[1][w]);
-    }
+    for (int w = 1; w < WPR; ++w) amax = fmax(amax, red64[w]);
   }
-
-  // Exact row maximum (unnormalized): the exact value of every element that
-  // could be the maximum. Candidates are kept as per-lane register bitmasks,
-  // so the loops below index no register array.
-  double amax_ex = (double)amax;
-  if (bmax > 0.f) {
-    const float thr = amax - 2.f * bmax;
-    double m_ex = 0.0;
-    auto scan = [&](auto uc) {
-      constexpr int U = decltype(uc)::value;
-      // units with no lane reaching the threshold hold no candidate
-      if (!__ballot(has[U] && umax[U] >= thr)) return;
-      uint32_t bits = 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) bits |= (uint32_t)(has[U] && fabsf(v[U][r]) >= thr) << r;
-      uint32_t rmask = or16(bits);  // registers that hold a candidate in some lane of this row
-      if (!__ballot(rmask != 0u)) return;
-      const Raw16<TIn> xin = inputs(uc);
-      while (rmask) {               // uniform over this 16-lane row
-        const int r = __builtin_ctz(rmask);
-        rmask &= rmask - 1;
-        uint32_t lmask = (uint32_t)(__ballot((bits >> r) & 1u) >> (16 * set)) & 0xFFFFu;
-        while (lmask) {
-          const int lc = __builtin_ctz(lmask);
-          lmask &= lmask - 1;
-          m_ex = fmax(m_ex, fabs(exact_elem(xin, true, lc + 16 * r, l16)));
-        }
-      }
-    };
-    scan(std::integral_constant<int, 0>{});
-    if constexpr (NU > 1) scan(std::integral_constant<int, 1>{});
-    if constexpr (NU > 2) scan(std::integral_constant<int, 2>{});
-    m_ex = wave_max(m_ex);
-    if constexpr (WPR > 1) {
-      if (lane == 0) red64[wave] = m_ex;
-      __syncthreads();
-      m_ex = red64[0];
-#pragma unroll
-      for (int w = 1; w < WPR; ++w) m_ex = fmax(m_ex, red64[w]);
-    }
-    amax_ex = m_ex;
-  }
-  const double unscale = rotate ? 0.0625 : 1.0;  // outputs above are 16 x the rotation (exact)
-  const float s = (float)(amax_ex * unscale / 127.0);
+  const double unscale = rotate ? 0.0625 : 1.0;  // the values above are 16 x the rotation (exact)
+  const float s = (float)(amax * unscale / 127.0);
   const double s64 = (double)s;
   const double inv64 = s > 0.0f ? 1.0 / s64 : 0.0;
-  const float inv = (float)(inv64 * unscale);  // applied to the unnormalized outputs
+  const double invu = inv64 * unscale;
+  constexpr double MAGIC = 6755399441055744.0;  // 1.5 * 2^52: adding it rounds to an integer (RNE)
+  // A normal s is within 2^-24 of amax / 127 (relative), so no quotient
+  // exceeds 127.5 and no code needs the clamp; a subnormal s can be much
+  // further off, and such rows take quant_code (which clamps) throughout.
+  const bool direct = s == 0.0f || s >= 0x1p-126f;
 
-  // Codes, one group at a time. f = v * inv + 1.5 * 2^23 in one fused
-  // rounding holds the nearest integer to the exact product v * inv in its
-  // low bits (two's complement in the low byte), and d = v * inv - (f - 1.5 *
-  // 2^23), again fused, its distance from that integer. A code is decided when
-  // |d| < lim: the fp32 transform (within bnd of the exact value, times inv),
-  // the rounding of inv and of d stay below 0.5 - lim, so the exact quotient
-  // rounds to the same integer, which is then within [-127, 127] (|exact| <=
-  // 127.5 - ...). A lane flag collects undecided codes; only a wave holding one
-  // rebuilds the per-element bits and takes the exact path (the reference
-  // rule on the exact value). A scale so small that inv overflows to
-  // infinity makes d NaN: such codes are undecided too.
   int8_t* qr = q + row * ldq;
-  auto codes = [&](auto uc) {
-    constexpr int U = decltype(uc)::value;
-    uint32_t code[16];
-    const float lim = 0.5f - (bnd[U] * inv * 1.0001f + 129.f * 0x1p-22f);
-    bool undecided = false;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float f = fmaf(v[U][r], inv, RQ_MAGIC);
-      const float d = fmaf(v[U][r], inv, RQ_MAGIC - f);
-      undecided |= !(fabsf(d) < lim);  // NaN (inv overflowed for a tiny scale): undecided
-      code[r] = __builtin_bit_cast(uint32_t, f);
-    }
-    if (__ballot(undecided && has[U])) {
-      uint32_t bits = 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float f = fmaf(v[U][r], inv, RQ_MAGIC);
-        const float d = fmaf(v[U][r], inv, RQ_MAGIC - f);
-        bits |= (uint32_t)(has[U] && !(fabsf(d) < lim)) << r;
-      }
-      uint32_t rmask = or16(bits);
-      const Raw16<TIn> xin = inputs(uc);
-      while (rmask) {  // uniform over this 16-lane row
-        const int r = __builtin_ctz(rmask);
-        rmask &= rmask - 1;
-        uint32_t lmask = (uint32_t)(__ballot((bits >> r) & 1u) >> (16 * set)) & 0xFFFFu;
-        while (lmask) {
-          const int lc = __builtin_ctz(lmask);
-          lmask &= lmask - 1;
-          const double xe = exact_elem(xin, rotate != 0, lc + 16 * r, l16);
-          const uint32_t c = (uint32_t)quant_code(xe * unscale, s64, inv64, 127.0);
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) code[rr] = (rr == r && l16 == lc) ? c : code[rr];
-        }
-      }
-    }
+  for (int u = 0; u < NU; ++u) {
     // element l16 + 16 r -> byte l16 + 16 r of this row's buffer, then 16
     // contiguous bytes per lane out
     wave_lds_sync();
+    bool tie = false;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mybuf[l16 + 16 * r] = (uint8_t)code[r];
+    for (int r = 0; r < 16; ++r) {
+      const double f = fma(v[u][r], invu, MAGIC);
+      const double d = fma(v[u][r], invu, MAGIC - f);
+      tie |= !(fabs(d) < 0.5 - 1e-9);
+      bbuf[l16 + 16 * r] = (uint8_t)__builtin_bit_cast(uint64_t, f);
+    }
+    if (__ballot((tie || !direct) && has[u])) {
+      // (recomputed from an opaque copy of invu: sharing the first pass's f
+      // and d would keep 64 registers live across the branch)
+      double invr = invu;
+      asm volatile("" : "+v"(invr));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const double f = fma(v[u][r], invr, MAGIC);
+        const double d = fma(v[u][r], invr, MAGIC - f);
+        if (!direct || !(fabs(d) < 0.5 - 1e-9))
+          bbuf[l16 + 16 * r] = (uint8_t)quant_code(v[u][r] * unscale, s64, inv64, 127.0);
+      }
+    }
     wave_lds_sync();
-    const uint4 w4 = *reinterpret_cast<const uint4*>(mybuf + 16 * l16);
-    if (has[U]) *reinterpret_cast<uint4*>(qr + (int64_t)(gb + set + 4 * U) * 256 + l16 * 16) = w4;
-  };
-  codes(std::integral_constant<int, 0>{});
-  if constexpr (NU > 1) codes(std::integral_constant<int, 1>{});
-  if constexpr (NU > 2) codes(std::integral_constant<int, 2>{});
+    const uint4 w4 = *reinterpret_cast<const uint4*>(bbuf + 16 * l16);
+    if (has[u]) *reinterpret_cast<uint4*>(qr + (int64_t)(gb + set + 4 * u) * 256 + l16 * 16) = w4;
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if (lane == 0 && (WPR == 1 || wave == 0)) scales[row] = s;
 }
 
@@ -766,16 +552,16 @@ static hipError_t rotate_from(const Src& src, TOut* y, int64_t ldy, int64_t m, i
   return hipGetLastError();
 }
 
-// int8 rows: the fast kernel up to 48 groups, the fp64 one above.
+// int8 rows: k_rotq_i8_d up to 48 groups, k_rotq_rows above.
 template <typename Src>
 static hipError_t rotq_i8_from(const Src& src, int64_t rows, int groups, int rot, int8_t* q8, int64_t ldq,
                                float* scales, hipStream_t stream) {
   const dim3 block(256);
   if (groups <= 12)
-    hipLaunchKernelGGL((k_rotq_i8_fast<Src, 1>), dim3((unsigned)((rows + 3) / 4)), block, 0, stream, src, rows,
+    hipLaunchKernelGGL((k_rotq_i8_d<Src, 1>), dim3((unsigned)((rows + 3) / 4)), block, 0, stream, src, rows,
                        groups, rot, q8, ldq, scales);
   else if (groups <= 48)
-    hipLaunchKernelGGL((k_rotq_i8_fast<Src, 4>), dim3((unsigned)rows), block, 0, stream, src, rows, groups, rot, q8,
+    hipLaunchKernelGGL((k_rotq_i8_d<Src, 4>), dim3((unsigned)rows), block, 0, stream, src, rows, groups, rot, q8,
                        ldq, scales);
   else
     hipLaunchKernelGGL((k_rotq_rows<Src, MODE_I8_ROW>), dim3((unsigned)((rows + 3) / 4)), block, 0, stream, src,

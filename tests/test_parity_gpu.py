@@ -194,16 +194,30 @@ def test_quantize_rows_int8(name, rows, rotate):
 
 
 def test_quantize_rows_zero_and_tiny_rows():
+    """Zero and tiny rows, and rows whose scale is a subnormal fp32 with few
+    significant bits: there s can sit several tenths of a percent away from
+    amax / 127, the largest quotient lands above 127.5 and the code must be
+    clamped to 127 (rows 6-11, single nonzero elements from 2e-40 to 2e-43,
+    fp32 and bf16 inputs, both widths of K)."""
     d = dev()
-    announce("tp_quantize_rows_int8 zero rows")
-    x = W.random_rows((6, 512), seed=11)
-    x[1] = 0.0
-    x[2] = 1e-30
-    x[3, 7] = -5.0
-    qa, sa = tp.tp_quantize_rows_int8(x.to(d))
-    rqa, rsa = oracle.quantize_activations_int8(f64(x))
-    assert np.array_equal(host(sa), rsa) and np.array_equal(host(qa), rqa)
-    assert host(sa)[1] == 0 and np.all(host(qa)[1] == 0)
+    announce("tp_quantize_rows_int8 zero, tiny and subnormal-scale rows")
+    for k in (512, 12288):
+        x = W.random_rows((12, k), seed=11)
+        x[1] = 0.0
+        x[2] = 1e-30
+        x[3, 7] = -5.0
+        for i, (val, col) in enumerate([(2e-40, 0), (-3.3e-41, 5), (7.1e-42, 300), (-2.2e-43, 17), (1.5e-40, 0),
+                                        (-9.9e-41, 511)]):
+            x[6 + i] = 0.0
+            x[6 + i, col] = val
+        for xin in (x, x.to(torch.bfloat16)):
+            qa, sa = tp.tp_quantize_rows_int8(xin.to(d))
+            rqa, rsa = oracle.quantize_activations_int8(f64(xin))
+            assert np.array_equal(host(sa), rsa), "scales differ"
+            assert np.array_equal(host(qa), rqa), f"{int(np.sum(host(qa) != rqa))} codes differ"
+            assert host(sa)[1] == 0 and np.all(host(qa)[1] == 0)
+        sub = host(sa)[6:]
+        assert np.any((sub > 0) & (sub < 2.0 ** -126)), "no subnormal scale was exercised"
 
 
 @pytest.mark.parametrize("k", [3072, 12288])
