@@ -417,6 +417,26 @@ struct SwigluSrc {
   }
 };
 
+// Largest magnitude of 16 doubles: a tree of v_max_f64 with both operands
+// taken as magnitudes (one instruction per pair; written out because the
+// compiler adds a canonicalizing max per element to fmax(., fabs(.))).
+__device__ __forceinline__ double absmax2(double a, double b) {
+  double r;
+  asm("v_max_f64 %0, |%1|, |%2|" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+__device__ __forceinline__ double absmax16(const double (&v)[16]) {
+  double m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m[i] = absmax2(v[2 * i], v[2 * i + 1]);
+#pragma unroll
+  for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) m[i] = absmax2(m[i], m[i + w]);  // operands already >= 0
+  return m[0];
+}
+
 // ------------------------- rotate and quantize rows to int8 (fp64 transform)
 // The same codes and scales as k_rotq_rows<MODE_I8_ROW> (the transform in
 // fp64, whose values are the exact ones whenever k_rotq_rows' are: every stage
@@ -484,8 +504,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     } else {
       transpose16(v[u], dbuf, l16);  // the same output order either way
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmax(amax, fabs(v[u][i]));
+    amax = fmax(amax, absmax16(v[u]));
     __builtin_amdgcn_sched_barrier(0);  // one group at a time: the next one's registers are not live yet
   }
   amax = wave_max(amax);  // rows without a group hold zeros
