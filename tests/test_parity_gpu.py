@@ -193,6 +193,27 @@ def test_quantize_rows_int8(name, rows, rotate):
     assert np.array_equal(host(qa), rqa), f"{int(np.sum(host(qa) != rqa))} codes differ"
 
 
+@pytest.mark.parametrize("groups", [1, 3, 5, 12, 13, 30, 47, 48, 49])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_quantize_rows_ragged_groups(groups, dt):
+    """Group counts that leave 16-lane rows of a wave without a group (fewer
+    than 4, or not a multiple of 4), split unevenly over the four waves of a
+    row (13 to 47 groups), fill every slot (12, 48), or take the one-wave-per-
+    row fp64 kernel above 48; 7 rows (not a multiple of the block's 4), with
+    outlier columns, rotated and not."""
+    d = dev()
+    k = 256 * groups
+    announce("tp_quantize_rows_int8 ragged groups", groups, dt)
+    x = W.random_rows((7, k), seed=groups + (100 if dt == "f32" else 0), dtype=dt)
+    x[:, min(5, k - 1)] *= 30.0
+    x[3] *= 1e-3
+    for rotate in (True, False):
+        qa, sa = tp.tp_quantize_rows_int8(x.to(d), rotate=rotate)
+        rqa, rsa = oracle.quantize_activations_int8(f64(x), rotate=rotate)
+        assert np.array_equal(host(sa).view(np.uint32), rsa.view(np.uint32)), "scales differ"
+        assert np.array_equal(host(qa), rqa), f"{int(np.sum(host(qa) != rqa))} codes differ"
+
+
 def test_quantize_rows_zero_and_tiny_rows():
     """Zero and tiny rows, and rows whose scale is a subnormal fp32 with few
     significant bits: there s can sit several tenths of a percent away from
