@@ -40,6 +40,10 @@
  *             from tp_last_error_message().
  * Results     Deterministic: the same inputs give the same output bytes (no
  *             atomics, fixed reduction orders).
+ * Values      Floating-point inputs are expected finite. A row or weight
+ *             holding NaN or infinity is not refused: its codes stay in the
+ *             code range and nothing faults, but its codes, scale and the
+ *             outputs that read it are unspecified.
  */
 #ifndef TP_H_
 #define TP_H_
