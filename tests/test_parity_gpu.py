@@ -241,6 +241,48 @@ def test_quantize_rows_zero_and_tiny_rows():
         assert np.any((sub > 0) & (sub < 2.0 ** -126)), "no subnormal scale was exercised"
 
 
+def test_non_finite_rows_stay_local():
+    """NaN and infinity are not refused (tp.h, Values): the rows holding them
+    get codes inside the code range and the calls succeed, while every other
+    row keeps the oracle's codes and scales bit for bit (rows are quantized
+    independently), for the activation quantizer and both weight widths."""
+    d = dev()
+    announce("non-finite rows: activation and weight quantizers")
+    for k in (3072, 12288):
+        x = W.random_rows((16, k), seed=13)
+        bad = {2: [(5, float("nan"))], 5: [(0, float("inf"))], 9: [(100, float("-inf")), (101, float("nan"))],
+               13: [(k - 1, float("nan"))]}
+        for r, cells in bad.items():
+            for c, v in cells:
+                x[r, c] = v
+        good = [r for r in range(16) if r not in bad]
+        for xin in (x, x.to(torch.bfloat16)):
+            qa, sa = tp.tp_quantize_rows_int8(xin.to(d))
+            torch.cuda.synchronize()
+            q = host(qa)
+            assert q.min() >= -127 and q.max() <= 127, "a code outside [-127, 127]"
+            rqa, rsa = oracle.quantize_activations_int8(f64(xin[good]))
+            assert np.array_equal(q[good], rqa), "a finite row's codes changed"
+            assert np.array_equal(host(sa)[good].view(np.uint32), rsa.view(np.uint32)), "a finite row's scale changed"
+    w = W.random_rows((24, 1024), seed=14)
+    w[3, 7] = float("nan")
+    w[10, 600] = float("inf")
+    w[17, 0] = float("-inf")
+    good = [r for r in range(24) if r not in (3, 10, 17)]
+    q8, s8 = tp.tp_rotate_quantize_weights(w.to(d), bits=8)
+    q4, s4 = tp.tp_rotate_quantize_weights(w.to(d), bits=4)
+    torch.cuda.synchronize()
+    c8 = host(q8)
+    assert c8.min() >= -127 and c8.max() <= 127
+    nib = host(q4).astype(np.int32)
+    lo, hi = ((nib & 0xF) ^ 8) - 8, (((nib >> 4) & 0xF) ^ 8) - 8
+    assert lo.min() >= -7 and lo.max() <= 7 and hi.min() >= -7 and hi.max() <= 7, "an int4 code outside [-7, 7]"
+    rq8, rs8 = oracle.quantize_weights_int8(w[good].numpy())
+    rq4, rs4 = oracle.quantize_weights_int4(w[good].numpy())
+    assert np.array_equal(c8[good], rq8) and np.array_equal(host(s8)[good].view(np.uint32), rs8.view(np.uint32))
+    assert np.array_equal(host(q4)[good], rq4) and np.array_equal(host(s4)[good].view(np.uint32), rs4.view(np.uint32))
+
+
 @pytest.mark.parametrize("k", [3072, 12288])
 def test_quantize_rows_exact_ties(k):
     """Every rotated value is a half-integer multiple of a power-of-two scale,
