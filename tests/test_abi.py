@@ -119,6 +119,30 @@ def test_rotate_quantize_empty_is_noop(lib):
     assert rq(lib, n=0) == 0
 
 
+def test_last_error_message_is_per_thread(lib):
+    """tp.h: the message belongs to the calling thread. Two threads are
+    refused for different reasons, one after the other, and each then reads
+    its own message."""
+    import threading
+    step = threading.Barrier(2)
+    got = {}
+
+    def worker(name, kw, status):
+        if name == "second":
+            step.wait()              # the first thread has been refused
+        assert rq(lib, **kw) == status
+        if name == "first":
+            step.wait()
+        step.wait()                  # both refused before either reads
+        got[name] = _err(lib)
+
+    t1 = threading.Thread(target=worker, args=("first", dict(bits=5), 7))
+    t2 = threading.Thread(target=worker, args=("second", dict(k=300, ldw=304, ldq=304), 3))
+    t1.start(); t2.start(); t1.join(); t2.join()
+    assert "bits" in got["first"] and "256" not in got["first"], got
+    assert "256" in got["second"] and "bits" not in got["second"], got
+
+
 # ------------------------------------------------------------- rotate rows
 def rr(lib, x=A, xd=1, m=8, k=512, ldx=512, y=B, yd=1, ldy=512):
     return lib.tp_hadamard_rotate_rows(x, xd, m, k, ldx, y, yd, ldy, None)
