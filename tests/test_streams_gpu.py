@@ -114,3 +114,29 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         _same(_outputs(b), want, f"replay {rep}")
     del graph
+
+
+def test_two_streams_at_once():
+    """Calls on two streams that share no output or workspace may overlap:
+    the W8A8 calls on one stream and the W4 call on another, issued together,
+    give the bytes of the calls run one after the other."""
+    d = dev()
+    announce("two streams at once")
+    b = _buffers(d)
+    _run(b)
+    torch.cuda.synchronize()
+    want = _outputs(b)
+    for k in ("qa", "y", "y40", "y4"):
+        b[k].zero_()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        tp.tp_quantize_rows_int8(b["x"], qa=b["qa"], sa=b["sa"], stream=s1)
+        tp.tp_qgemm_w8a8_prequantized(b["qa"], b["sa"], b["q8"], b["s8"], out=b["y"], workspace=b["ws"], stream=s1)
+        tp.tp_qgemm_w8a8_prequantized(b["qa"][:40], b["sa"][:40], b["q8"], b["s8"], out=b["y40"],
+                                      workspace=b["ws40"], stream=s1)
+        tp.tp_qgemm_w4(b["x4"], b["q4"], b["s4"], rotate=True, out=b["y4"], workspace=b["ws4"], stream=s2)
+    s1.synchronize()
+    s2.synchronize()
+    _same(_outputs(b), want, "two streams")
