@@ -23,13 +23,20 @@ from tests.gpu_util import announce, dev, f64, host, sample_rows
 pytestmark = pytest.mark.gpu
 
 
-def _weights(wl, bits, rows=None):
+_CODES = {}
+
+
+def _weights(wl, bits):
+    """The oracle's own codes and scales of a workload weight (no oracle
+    input comes from the device), on the device for the call under test."""
     d = dev()
-    _, w = W.generate(wl, rows=1)
-    if rows is not None:
-        w = w[:rows]
-    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=bits)
-    return q, s
+    key = (wl, bits)
+    if key not in _CODES:
+        _, w = W.generate(wl, rows=1)
+        wn = w.float().numpy()
+        _CODES[key] = oracle.quantize_weights_int8(wn) if bits == 8 else oracle.quantize_weights_int4(wn)
+    q, s = _CODES[key]
+    return torch.from_numpy(q).to(d), torch.from_numpy(s).to(d)
 
 
 def _bf16_bits(x64):
@@ -84,8 +91,7 @@ def test_loader_ragged_and_views():
     d = dev()
     announce("loader padded views, ragged rows")
     wl = W.TINY.with_(n=37, k=1280, seed=5)
-    _, w = W.generate(wl, rows=1)
-    q, s = tp.tp_rotate_quantize_weights(w.to(d), bits=4)
+    q, s = _weights(wl, 4)
     qbuf = torch.zeros((40, 640 + 64), dtype=torch.uint8, device=d)
     qbuf[1:38, 16:656] = q
     out = torch.full((39, 1280 + 32), 3.0, dtype=torch.float32, device=d)

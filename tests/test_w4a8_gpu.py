@@ -23,6 +23,17 @@ from tests.gpu_util import announce, dev, f64, host, sample_rows
 
 pytestmark = pytest.mark.gpu
 
+_W4 = {}
+
+
+def _weights4(key, w, d):
+    """The oracle's own int4 codes and group scales of w (no oracle input
+    comes from the device), on the device for the product under test."""
+    if key not in _W4:
+        _W4[key] = oracle.quantize_weights_int4(w.float().numpy())
+    rq4, rs4 = _W4[key]
+    return rq4, rs4, torch.from_numpy(rq4).to(d), torch.from_numpy(rs4).to(d)
+
 
 def _check(y_dev, y, acc, s, sa, what, bf16=False):
     g = acc.shape[0]
@@ -40,17 +51,17 @@ def _check(y_dev, y, acc, s, sa, what, bf16=False):
 def _case(wl, sel=None, out_dtype=torch.float32, rotate=True):
     d = dev()
     x, w = W.generate(wl, rows=None)
-    q4, s4 = tp.tp_rotate_quantize_weights(w.to(d), bits=4)
+    rq4, rs4, q4, s4 = _weights4(wl, w, d)
     y, qa, sa = tp.tp_qgemm_w4a8(x.to(d), q4, s4, rotate=rotate, out_dtype=out_dtype, want_codes=True)
     x64 = f64(x) if sel is None else f64(x)[sel]
-    ry, racc, rqa, rsa = oracle.qgemm_w4a8(x64, host(q4), host(s4), rotate=rotate)
+    ry, racc, rqa, rsa = oracle.qgemm_w4a8(x64, rq4, rs4, rotate=rotate)
     gq, gs = host(qa), host(sa)
     if sel is not None:
         gq, gs = gq[sel], gs[sel]
     assert np.array_equal(gs, rsa), "activation scales"
     assert np.array_equal(gq, rqa), "activation codes"
     yd = f64(y) if sel is None else f64(y)[sel]
-    _check(yd, ry, racc, host(s4), rsa, wl.name, bf16=out_dtype == torch.bfloat16)
+    _check(yd, ry, racc, rs4, rsa, wl.name, bf16=out_dtype == torch.bfloat16)
     return y
 
 
@@ -81,10 +92,12 @@ def test_w4a8_bf16_out_and_prerotated():
     d = dev()
     x, w = W.generate(wl)
     xr = tp.tp_hadamard_rotate_rows(x.to(d), out_dtype=torch.bfloat16)
-    q4, s4 = tp.tp_rotate_quantize_weights(w.to(d), bits=4)
+    rq4, rs4, q4, s4 = _weights4(wl, w, d)
     y = tp.tp_qgemm_w4a8(xr, q4, s4, rotate=False, out_dtype=torch.bfloat16)
-    ry, racc, _, rsa = oracle.qgemm_w4a8(f64(xr), host(q4), host(s4), rotate=False)
-    _check(f64(y), ry, racc, host(s4), rsa, "bf16 out", bf16=True)
+    # the device's rotated bf16 rows are this call's input (the rotation is
+    # checked against the oracle in the rotation tests)
+    ry, racc, _, rsa = oracle.qgemm_w4a8(f64(xr), rq4, rs4, rotate=False)
+    _check(f64(y), ry, racc, rs4, rsa, "bf16 out", bf16=True)
 
 
 def test_w4a8_from_fused_ffn_middle():
@@ -97,14 +110,14 @@ def test_w4a8_from_fused_ffn_middle():
     g, u = W.gate_up(fm)
     qa, sa = tp.tp_swiglu_rotate(g.to(d), u.to(d), out_kind="i8")
     _, w = W.generate(W.DIT_DOWN, rows=1)
-    q4, s4 = tp.tp_rotate_quantize_weights(w.to(d), bits=4)
+    rq4, rs4, q4, s4 = _weights4(W.DIT_DOWN, w, d)
     y = tp.tp_qgemm_w4a8_prequantized(qa, sa, q4, s4)
     rqa, rsa = oracle.ffn_middle_int8(f64(g), f64(u))
     assert np.array_equal(host(qa), rqa) and np.array_equal(host(sa), rsa)
-    q = oracle.unpack_int4(host(q4))
+    q = oracle.unpack_int4(rq4)
     acc = oracle.group_accumulate(rqa, q)
-    ry = np.einsum("gmn,gn->mn", acc.astype(np.float64), host(s4).astype(np.float64).T) * rsa.astype(np.float64)[:, None]
-    _check(f64(y), ry, acc, host(s4), rsa, "fused middle -> w4a8")
+    ry = np.einsum("gmn,gn->mn", acc.astype(np.float64), rs4.astype(np.float64).T) * rsa.astype(np.float64)[:, None]
+    _check(f64(y), ry, acc, rs4, rsa, "fused middle -> w4a8")
 
 
 def test_w4a8_padded_views_and_determinism():
@@ -113,7 +126,7 @@ def test_w4a8_padded_views_and_determinism():
     wl = W.PROJ256.with_(name="w4a8_views", m=40, n=520, k=2048, seed=33, path="w4a8")
     x, w = W.generate(wl)
     qa, sa = tp.tp_quantize_rows_int8(x.to(d))
-    q4, s4 = tp.tp_rotate_quantize_weights(w.to(d), bits=4)
+    rq4, rs4, q4, s4 = _weights4(wl, w, d)
     cbuf = torch.full((44, 520 + 16), 9.0, dtype=torch.float32, device=d)
     out = cbuf[2:42, 8:528]
     y1 = tp.tp_qgemm_w4a8_prequantized(qa, sa, q4, s4, out=out).clone()
@@ -121,6 +134,6 @@ def test_w4a8_padded_views_and_determinism():
     assert torch.equal(y1, y2), "repeat runs differ"
     assert torch.all(cbuf[:2] == 9.0) and torch.all(cbuf[42:] == 9.0)
     assert torch.all(cbuf[:, :8] == 9.0) and torch.all(cbuf[:, 528:] == 9.0)
-    ry, racc, rqa, rsa = oracle.qgemm_w4a8(f64(x), host(q4), host(s4))
+    ry, racc, rqa, rsa = oracle.qgemm_w4a8(f64(x), rq4, rs4)
     assert np.array_equal(host(qa), rqa)
-    _check(f64(y1), ry, racc, host(s4), rsa, "padded views")
+    _check(f64(y1), ry, racc, rs4, rsa, "padded views")
