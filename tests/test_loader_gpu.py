@@ -53,7 +53,8 @@ def test_dequantize_unrotate(bits, dt, name):
     odt = torch.float32 if dt == "f32" else torch.bfloat16
     w = tp.tp_dequantize_unrotate(q, s, bits, out_dtype=odt)
     sel = sample_rows(wl.n, 64, seed=3) if wl.n > 512 else np.arange(wl.n)
-    ref = oracle.dequantize_unrotate(host(q)[sel], host(s)[sel], bits)
+    rqn, rsn = _CODES[(wl, bits)]
+    ref = oracle.dequantize_unrotate(rqn[sel], rsn[sel], bits)
     want = ref.astype(np.float32).astype(np.float64) if dt == "f32" else _bf16_bits(ref)
     got = f64(w)[sel]
     assert np.array_equal(got, want), f"{int(np.sum(got != want))} elements differ"
@@ -67,7 +68,8 @@ def test_requantize(bits_in, bits_out, name):
     q, s = _weights(wl, bits_in)
     qo, so = tp.tp_requantize_weights(q, s, bits_in, bits_out)
     sel = sample_rows(wl.n, 64, seed=4) if wl.n > 512 else np.arange(wl.n)
-    rq, rs = oracle.requantize(host(q)[sel], host(s)[sel], bits_in, bits_out)
+    rqn, rsn = _CODES[(wl, bits_in)]
+    rq, rs = oracle.requantize(rqn[sel], rsn[sel], bits_in, bits_out)
     assert np.array_equal(host(so)[sel], rs), "scales"
     assert np.array_equal(host(qo)[sel], rq), "codes"
     if bits_in == bits_out:
@@ -96,12 +98,13 @@ def test_loader_ragged_and_views():
     qbuf[1:38, 16:656] = q
     out = torch.full((39, 1280 + 32), 3.0, dtype=torch.float32, device=d)
     tp.tp_dequantize_unrotate(qbuf[1:38, 16:656], s, 4, out=out[1:38, 16:1296])
-    ref = oracle.dequantize_unrotate(host(q), host(s), 4).astype(np.float32)
+    rqn, rsn = _CODES[(wl, 4)]
+    ref = oracle.dequantize_unrotate(rqn, rsn, 4).astype(np.float32)
     assert np.array_equal(host(out[1:38, 16:1296]), ref)
     assert torch.all(out[0] == 3.0) and torch.all(out[38] == 3.0) and torch.all(out[:, :16] == 3.0)
     q8 = torch.zeros((37, 1280 + 128), dtype=torch.int8, device=d)
     s8 = torch.zeros((41,), dtype=torch.float32, device=d)
     tp.tp_requantize_weights(qbuf[1:38, 16:656], s, 4, 8, q_out=q8[:, 64:1344], scales_out=s8[4:41])
-    rq, rs = oracle.requantize(host(q), host(s), 4, 8)
+    rq, rs = oracle.requantize(rqn, rsn, 4, 8)
     assert np.array_equal(host(q8[:, 64:1344]), rq) and np.array_equal(host(s8[4:41]), rs)
     assert torch.all(q8[:, :64] == 0) and torch.all(s8[:4] == 0)

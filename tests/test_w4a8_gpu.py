@@ -91,12 +91,12 @@ def test_w4a8_bf16_out_and_prerotated():
     wl = W.PROJ256.with_(name="w4a8_pre", m=300, n=700, k=1536, seed=31, path="w4a8")
     d = dev()
     x, w = W.generate(wl)
-    xr = tp.tp_hadamard_rotate_rows(x.to(d), out_dtype=torch.bfloat16)
+    # pre-rotated bf16 rows made by the oracle, the input of both sides
+    xr64 = oracle.bf16_round(oracle.rotate_groups(f64(x)))
+    xr = torch.from_numpy(xr64.astype(np.float32)).to(torch.bfloat16).to(d)  # exact: bf16 values
     rq4, rs4, q4, s4 = _weights4(wl, w, d)
     y = tp.tp_qgemm_w4a8(xr, q4, s4, rotate=False, out_dtype=torch.bfloat16)
-    # the device's rotated bf16 rows are this call's input (the rotation is
-    # checked against the oracle in the rotation tests)
-    ry, racc, _, rsa = oracle.qgemm_w4a8(f64(xr), rq4, rs4, rotate=False)
+    ry, racc, _, rsa = oracle.qgemm_w4a8(xr64, rq4, rs4, rotate=False)
     _check(f64(y), ry, racc, rs4, rsa, "bf16 out", bf16=True)
 
 
